@@ -1,0 +1,10 @@
+"""Run every oracle pin (tests/oracle_pins.py) against the oracle (CPU)."""
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin(oracle.default())
