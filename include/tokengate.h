@@ -1,0 +1,200 @@
+/*
+ * tokengate.h -- C ABI of the token-gated prefill path on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * TokenGate (pages: "TokenGate: Adapting LLMs for Fast and Memory-Efficient
+ * Prefill with Learned Token Pruning", ai.info summary; the techbycountry
+ * explainer "TokenGate Learned Token Pruning LLM Prefill Explained"; the
+ * README mirror "TokenGate: Adapting LLMs for pre-fill with learned skimming
+ * for ~11x speedup") inserts a small gate at one layer L of a trained
+ * transformer.  The gate scores every prunable token of the prompt, keeps the
+ * K best plus every non-prunable token, and the layers above L run only on
+ * the kept tokens, with the gate score added as a per-key, per-head bias to
+ * their attention logits.  This library is that path's hot core:
+ *
+ *   tg_gate_score      RMSNorm + MLP scorer over the residual rows   [a1]
+ *   tg_topk_select     top-K selection and ordered compaction        [a2,a3]
+ *   tg_compact_gather  gather of residual rows/positions/scores      [a4]
+ *   tg_bias_attn_fwd   causal GQA attention with the gate bias       [a5]
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every data pointer is DEVICE memory owned by the caller.  The library
+ *   allocates nothing and keeps no per-call state; the only scratch memory
+ *   is the caller-provided workspace of tg_topk_select.
+ * - Every call only enqueues work on `stream` (a hipStream_t; NULL means the
+ *   null stream) and returns; nothing synchronises the device and nothing
+ *   is read back to the host.  Results are valid once the stream reaches
+ *   them.
+ * - Errors are return codes.  All shape, dtype, pointer and alignment
+ *   checks run on the host BEFORE any device work, so a call that returns
+ *   anything but TG_OK has enqueued nothing (except TG_ERR_LAUNCH).  The
+ *   library never aborts and never throws across this boundary.
+ *   tg_last_error() returns a thread-local description of the last failure.
+ * - Sizes are int64_t; token counts must fit in int32 (T <= 2^31 - 1).
+ * - "bf16" is bfloat16 (1-8-7), "f32" is IEEE binary32; matrices are
+ *   row-major with the stated row strides in ELEMENTS.
+ */
+#ifndef TOKENGATE_H
+#define TOKENGATE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tg_status {
+  TG_OK = 0,
+  TG_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative or inconsistent size, misalignment */
+  TG_ERR_UNSUPPORTED = 2,      /* valid request outside what the kernels implement */
+  TG_ERR_WORKSPACE = 3,        /* workspace missing or smaller than tg_topk_workspace_size() */
+  TG_ERR_LAUNCH = 4            /* the HIP runtime refused a kernel launch */
+} tg_status;
+
+typedef enum tg_dtype { TG_DTYPE_F32 = 0, TG_DTYPE_BF16 = 1 } tg_dtype;
+
+/* Static, never-NULL name of a status code. */
+const char* tg_status_str(int status);
+
+/* Thread-local, human-readable detail of the last failed call on this
+ * thread ("" if none).  Valid until the next call on the same thread. */
+const char* tg_last_error(void);
+
+/* --------------------------------------------------------------------------
+ * [a1] Gate scorer.  Pages: ai.info summary "Key Contributions" item 1 (a
+ * scoring MLP over each token's RMSNorm-normalised post-attention residual
+ * scores the prunable tokens) and the README mirror "How it works".
+ *
+ *   for prunable t:  u = gamma * x_t / sqrt(mean_i x_{t,i}^2 + eps)
+ *                    s_t = b2 + sum_j w2_j * SiLU((W1 u)_j + b1_j)
+ *   otherwise:       s_t = 0   (non-prunable tokens are never pruned, so
+ *                               they carry no gate bias)
+ *
+ * dt          TG_DTYPE_BF16 or TG_DTYPE_F32: dtype of resid and w1.  The
+ *             bf16 path multiplies on bf16 MFMA with fp32 accumulation; the
+ *             f32 path is fp32 throughout.
+ * T, d, h     tokens, hidden size, gate MLP width.  T >= 0 (T == 0 is a
+ *             no-op), d >= 1, h >= 1.  bf16 path: d % 8 == 0 and
+ *             h in {64, 128, 192, 256}.
+ * resid       [T][resid_row_stride] of dt; row t's first d elements are x_t.
+ *             bf16 path: resid and resid_row_stride*2 16-byte aligned.
+ * prunable    [T] bytes, nonzero = prunable.
+ * rms_weight  [d] f32 RMSNorm weight gamma, or NULL for all ones.
+ * eps         >= 0.
+ * w1          [h][d] of dt (Linear layout), 16-byte aligned on the bf16 path.
+ * b1          [h] f32 or NULL (zeros).  w2 [h] f32.  b2 scalar.
+ * scores      out [T] f32.
+ * ------------------------------------------------------------------------ */
+tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                        const void* resid, int64_t resid_row_stride,
+                        const uint8_t* prunable, const float* rms_weight,
+                        float eps, const void* w1, const float* b1,
+                        const float* w2, float b2, float* scores,
+                        void* stream);
+
+/* --------------------------------------------------------------------------
+ * [a2, a3] Top-K selection and order-preserving compaction.  Pages: ai.info
+ * summary "Key Contributions" item 1 and "Methodology in Plain English": the
+ * K highest-scoring prunable tokens plus ALL non-prunable tokens continue
+ * upward; the README "Quick start" budget K = None keeps every prunable
+ * token.
+ *
+ * Kept set = { t : !prunable[t] }  U  the first min(K, |P|) prunable tokens
+ * ordered by (score descending, index ascending).  Scores compare as fp32
+ * values: -0 == +0, +-inf are ordinary values, NaN ranks below every
+ * number (NaNs tie, lower index first).  kept_idx lists the kept tokens in
+ * ascending original order, so its length is N = min(K, |P|) + |not P|.
+ *
+ * T              tokens, 0 <= T <= 2^31 - 1.
+ * scores         [T] f32 (values at non-prunable positions are ignored).
+ * prunable       [T] bytes, nonzero = prunable.
+ * K              budget, K >= 0.  K >= |P| keeps every token; K = 0 keeps
+ *                only the non-prunable tokens.
+ * kept_idx       out, [kept_capacity] int32.  Entries beyond the kept count
+ *                are left untouched; kept entries at positions >=
+ *                kept_capacity are dropped (so a capacity of T is always
+ *                enough).
+ * n_kept         out, [1] int32 on the device: the kept count N (may exceed
+ *                kept_capacity, which signals a too-small capacity).
+ * workspace      device scratch of at least tg_topk_workspace_size(T) bytes,
+ *                256-byte aligned.  It must be all-zero before its first use;
+ *                every call leaves it all-zero again when its kernels finish.
+ *                Calls sharing a workspace must be ordered on one stream.
+ * ------------------------------------------------------------------------ */
+size_t tg_topk_workspace_size(int64_t T);
+
+tg_status tg_topk_select(int64_t T, const float* scores,
+                         const uint8_t* prunable, int64_t K,
+                         int32_t* kept_idx, int64_t kept_capacity,
+                         int32_t* n_kept, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
+ * [a4] Gather into kept order.  Pages: ai.info summary "Key Contributions"
+ * item 1 and the README mirror "How it works": layers above the gate
+ * process, and keep KV entries for, only the kept tokens.
+ *
+ *   resid_kept[r][:] = resid[kept_idx[r]][:]   (bit copy of d elements)
+ *   pos_kept[r]      = kept_idx[r]             (original position)
+ *   score_kept[r]    = scores[kept_idx[r]]     (bit copy)
+ *
+ * T            rows in resid (bounds for kept_idx).  N >= 0 kept rows
+ *              (N == 0 is a no-op).  d >= 1.
+ * resid        [T][resid_row_stride] of dt.  resid_kept [N][kept_row_stride].
+ *              Both pointers and both strides (in bytes) 16-byte aligned,
+ *              resid_kept may be NULL (no rows copied).
+ * scores       [T] f32; may be NULL only if score_kept is NULL.
+ * kept_idx     [N] int32.  An index outside [0, T) yields a zero row,
+ *              pos_kept = -1 and score_kept = 0 for that r (no fault).
+ * pos_kept, score_kept   out [N], each may be NULL.
+ * ------------------------------------------------------------------------ */
+tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
+                            const void* resid, int64_t resid_row_stride,
+                            const float* scores, const int32_t* kept_idx,
+                            void* resid_kept, int64_t kept_row_stride,
+                            int32_t* pos_kept, float* score_kept,
+                            void* stream);
+
+/* --------------------------------------------------------------------------
+ * [a5] Token-gated attention, forward.  Pages: ai.info summary "Key
+ * Contributions" items 2 and 3 and "Methodology in Plain English": each kept
+ * key's gate score, times a per-layer per-head gain, is added to the
+ * attention logits of the upper layers before the online softmax; a
+ * per-query temperature (driven by the ratio of the query's original
+ * position to its rank among kept tokens) rescales the logits.
+ *
+ * For query row r, query head h, key c (c <= r when causal),
+ *   kv = h / (Hq / Hkv)
+ *   z  = q_scale[r] * ( softmax_scale * <Q[r,h,:], K[c,kv,:]> + gain[h] * key_score[c] )
+ *   O[r,h,:] = sum_c softmax_c(z) * V[c,kv,:],   lse[h][r] = log sum_c exp(z)
+ * A row whose logits are all -inf gets O = 0 and lse = -inf.
+ *
+ * dt            TG_DTYPE_BF16 (bf16 MFMA, fp32 softmax) or TG_DTYPE_F32.
+ * N             kept tokens, 0 <= N <= 2^31 - 1 (N == 0 is a no-op).
+ * Hq, Hkv       query / KV heads, Hkv >= 1, Hq % Hkv == 0.
+ * D             head dim: 64 or 128.
+ * q             [N][Hq][D] of dt, contiguous.  k, v: [N][Hkv][D] of dt.
+ *               16-byte aligned.
+ * key_score     [N] f32 gate scores of the kept tokens, or NULL for no bias
+ *               (plain attention; gain is then ignored).
+ * gain          [Hq] f32, required when key_score != NULL.  Expected > 0
+ *               (a softplus output); gain 0 with an infinite score is NaN.
+ * q_scale       [N] f32 per-query logit scale, or NULL for all ones.
+ *               Expected > 0.
+ * softmax_scale <= 0 selects 1/sqrt(D).
+ * causal        nonzero: key c is visible to query r only if c <= r.
+ * out           out [N][Hq][D] of dt.  lse: out [Hq][N] f32, or NULL.
+ * ------------------------------------------------------------------------ */
+tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                           int64_t D, const void* q, const void* k,
+                           const void* v, const float* key_score,
+                           const float* gain, const float* q_scale,
+                           float softmax_scale, int causal, void* out,
+                           float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TOKENGATE_H */

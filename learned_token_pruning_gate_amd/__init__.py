@@ -1,0 +1,247 @@
+"""Token-gated prefill path for AMD Instinct MI355X (gfx950).
+
+Thin Python binding over ``libtokengate.so`` (C ABI in ``include/tokengate.h``).
+This module only marshals arguments: PyTorch supplies device memory and the
+stream, and every step of the path runs in the library's HIP kernels.  There
+is no CPU fallback: if the library is missing, or a tensor is not on the
+GPU, the call raises.
+
+Entry points (same names as the C ABI):
+
+* ``tg_gate_score``       -- RMSNorm + MLP scorer over the residual rows
+* ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
+* ``tg_compact_gather``   -- gather of rows, positions and scores
+* ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "TokenGateError", "lib_path", "load", "kept_count",
+    "tg_status_str", "tg_last_error", "tg_gate_score", "tg_topk_workspace_size",
+    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
+    "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
+    "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libtokengate.so")
+
+TG_OK, TG_ERR_INVALID_ARGUMENT, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_LAUNCH = range(5)
+TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
+
+EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_topk_workspace_size",
+            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd")
+
+
+class TokenGateError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__("%s: %s: %s" % (where, _status_name(status), detail))
+
+
+_lib = None
+
+
+def load():
+    """Load libtokengate.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(
+            "libtokengate.so is not built (%s); run "
+            "`python learned_token_pruning_gate_amd/build.py`" % lib_path)
+    lib = ctypes.CDLL(lib_path)
+    P, I64, F, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    lib.tg_status_str.argtypes = [I]
+    lib.tg_status_str.restype = ctypes.c_char_p
+    lib.tg_last_error.argtypes = []
+    lib.tg_last_error.restype = ctypes.c_char_p
+    lib.tg_gate_score.argtypes = [I, I64, I64, I64, P, I64, P, P, F, P, P, P, F, P, P]
+    lib.tg_gate_score.restype = I
+    lib.tg_topk_workspace_size.argtypes = [I64]
+    lib.tg_topk_workspace_size.restype = ctypes.c_size_t
+    lib.tg_topk_select.argtypes = [I64, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]
+    lib.tg_topk_select.restype = I
+    lib.tg_compact_gather.argtypes = [I, I64, I64, I64, P, I64, P, P, P, I64, P, P, P]
+    lib.tg_compact_gather.restype = I
+    lib.tg_bias_attn_fwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P]
+    lib.tg_bias_attn_fwd.restype = I
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    return load().tg_status_str(int(s)).decode()
+
+
+def tg_status_str(status: int) -> str:
+    return _status_name(status)
+
+
+def tg_last_error() -> str:
+    return load().tg_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != TG_OK:
+        raise TokenGateError(status, where, tg_last_error())
+
+
+def _dev(t, name, dtype=None, allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return TG_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return TG_DTYPE_F32
+    raise TypeError("unsupported dtype %s (bf16 or f32)" % t.dtype)
+
+
+def kept_count(n_prunable: int, T: int, K: int) -> int:
+    """N = min(K, |P|) + |not P|: the number of kept tokens."""
+    return min(int(K), int(n_prunable)) + (int(T) - int(n_prunable))
+
+
+# ---------------------------------------------------------------------------
+def tg_gate_score(resid, prunable, w1, w2, b2=0.0, rms_weight=None, b1=None, eps=1e-6,
+                  scores=None, stream=None):
+    """scores[T] (f32) for resid [T, d] (bf16 or f32, row stride >= d)."""
+    lib = load()
+    _dev(resid, "resid")
+    T, d = resid.shape
+    if resid.stride(1) != 1:
+        raise ValueError("resid rows must be contiguous")
+    _dev(prunable, "prunable", torch.uint8)
+    _dev(w1, "w1", resid.dtype)
+    h = w1.shape[0]
+    if tuple(w1.shape) != (h, d) or not w1.is_contiguous():
+        raise ValueError("w1 must be a contiguous [h, d] tensor")
+    _dev(w2, "w2", torch.float32)
+    _dev(rms_weight, "rms_weight", torch.float32, allow_none=True)
+    _dev(b1, "b1", torch.float32, allow_none=True)
+    if scores is None:
+        scores = torch.empty(T, dtype=torch.float32, device=resid.device)
+    _dev(scores, "scores", torch.float32)
+    st = lib.tg_gate_score(_dt(resid), T, d, h, _ptr(resid), resid.stride(0), _ptr(prunable),
+                           _ptr(rms_weight), float(eps), _ptr(w1), _ptr(b1), _ptr(w2),
+                           float(b2), _ptr(scores), _stream(stream))
+    _check(st, "tg_gate_score")
+    return scores
+
+
+def tg_topk_workspace_size(T: int) -> int:
+    return int(load().tg_topk_workspace_size(int(T)))
+
+
+def tg_topk_select(scores, prunable, K, kept_idx=None, n_kept=None, workspace=None,
+                   stream=None):
+    """(kept_idx, n_kept): kept_idx has capacity T unless given; its first N
+    entries are the kept tokens in ascending order; n_kept is a 1-element
+    int32 device tensor holding N.  ``workspace`` (uint8, zero-initialised
+    once) may be reused across calls on one stream."""
+    lib = load()
+    _dev(scores, "scores", torch.float32)
+    _dev(prunable, "prunable", torch.uint8)
+    T = scores.shape[0]
+    dev = scores.device
+    if kept_idx is None:
+        kept_idx = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    _dev(kept_idx, "kept_idx", torch.int32)
+    if n_kept is None:
+        n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    _dev(n_kept, "n_kept", torch.int32)
+    need = tg_topk_workspace_size(T)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib.tg_topk_select(T, _ptr(scores), _ptr(prunable), int(K), _ptr(kept_idx),
+                            kept_idx.numel(), _ptr(n_kept), _ptr(workspace),
+                            workspace.numel(), _stream(stream))
+    _check(st, "tg_topk_select")
+    return kept_idx, n_kept
+
+
+def tg_compact_gather(resid, scores, kept_idx, N, resid_kept=None, pos_kept=None,
+                      score_kept=None, stream=None):
+    """(resid_kept [N, d], pos_kept [N] int32, score_kept [N] f32)."""
+    lib = load()
+    _dev(resid, "resid")
+    T, d = resid.shape
+    _dev(scores, "scores", torch.float32)
+    _dev(kept_idx, "kept_idx", torch.int32)
+    N = int(N)
+    if N > kept_idx.numel():
+        raise ValueError("N exceeds kept_idx")
+    dev = resid.device
+    if resid_kept is None:
+        resid_kept = torch.empty((N, d), dtype=resid.dtype, device=dev)
+    if pos_kept is None:
+        pos_kept = torch.empty(N, dtype=torch.int32, device=dev)
+    if score_kept is None:
+        score_kept = torch.empty(N, dtype=torch.float32, device=dev)
+    _dev(resid_kept, "resid_kept", resid.dtype)
+    _dev(pos_kept, "pos_kept", torch.int32)
+    _dev(score_kept, "score_kept", torch.float32)
+    st = lib.tg_compact_gather(_dt(resid), T, N, d, _ptr(resid), resid.stride(0),
+                               _ptr(scores), _ptr(kept_idx), _ptr(resid_kept),
+                               resid_kept.stride(0), _ptr(pos_kept), _ptr(score_kept),
+                               _stream(stream))
+    _check(st, "tg_compact_gather")
+    return resid_kept, pos_kept, score_kept
+
+
+def tg_bias_attn_fwd(q, k, v, key_score, gain, q_scale=None, softmax_scale=0.0, causal=True,
+                     out=None, lse=None, want_lse=True, stream=None):
+    """(out [N, Hq, D], lse [Hq, N] or None)."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, n, q.dtype)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    N, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (N, Hkv, D) or tuple(v.shape) != (N, Hkv, D):
+        raise ValueError("k and v must be [N, Hkv, D]")
+    _dev(key_score, "key_score", torch.float32, allow_none=True)
+    _dev(gain, "gain", torch.float32, allow_none=True)
+    _dev(q_scale, "q_scale", torch.float32, allow_none=True)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", q.dtype)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
+    _dev(lse, "lse", torch.float32, allow_none=True)
+    st = lib.tg_bias_attn_fwd(_dt(q), N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v),
+                              _ptr(key_score), _ptr(gain), _ptr(q_scale),
+                              float(softmax_scale), 1 if causal else 0, _ptr(out), _ptr(lse),
+                              _stream(stream))
+    _check(st, "tg_bias_attn_fwd")
+    return out, lse

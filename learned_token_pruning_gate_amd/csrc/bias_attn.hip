@@ -1,0 +1,462 @@
+// bias_attn.hip -- [a5] token-gated attention forward: causal GQA flash
+// attention over the kept tokens with a per-head, per-key additive gate
+// bias and an optional per-query logit scale.
+//
+// TokenGate pages: ai.info summary "Key Contributions" items 2 and 3 and
+// "Methodology in Plain English" -- each kept key's importance score, times
+// a learned per-layer per-head gain, is added to the attention logits of
+// every upper layer before the online softmax; a learned temperature driven
+// by the ratio of a query's position to its rank among kept tokens rescales
+// the logits.  The pages' own kernel is a patched FlashAttention-2 for
+// NVIDIA parts; this is a gfx950 design of its own.
+//
+//   z[r,c] = c_r * (scale * <q_r, k_c> + gain_h * score_c),   c <= r
+//
+// bf16 path (gfx950, wave64):
+//   * A workgroup (4 waves) owns one KV head and a block of query positions;
+//     each wave owns 32 query positions of one query head, and the HPW query
+//     heads of the group that share the KV head reuse every K/V tile staged
+//     in LDS.
+//   * Logits are computed transposed, S^T = K Q^T, on
+//     v_mfma_f32_32x32x16_bf16: in the accumulator each lane holds one
+//     query column and 16 keys of a 32-key block, so the running max and
+//     sum of a query stay inside the lane (plus one exchange between the
+//     two lane halves), and the probabilities P^T, converted to bf16 in
+//     place, are exactly the B operand of the next product O^T += V^T P^T.
+//     The keys that the accumulator layout puts in a lane's k-slots are
+//     matched by reading V^T from LDS in the same order.
+//   * Q stays in registers for the whole key loop.  K tiles are staged in
+//     LDS row-major (padded); V tiles are transposed on their way into LDS
+//     (4 keys x 8 dims per thread, packed with byte permutes).  The next
+//     tile's global loads are issued before the current tile's math.
+//   * The bias gain_h*log2(e)*score_c is formed once per key tile and head
+//     in LDS; logits use exp2 with log2(e) folded into the scale; the output
+//     is rescaled only when some query's running max grows.
+//   * Workgroups are ordered longest-first (causal) and the KV head is the
+//     fastest-varying index, so consecutive workgroups -- which the
+//     dispatcher spreads over the 8 XCDs -- keep one KV head per XCD L2.
+//
+// f32 path: one thread per (query, head), fp32 online softmax.
+#include "tg_common.hpp"
+
+namespace tg {
+namespace {
+
+constexpr int kBK = 64;           // keys per tile
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+template <int D>
+struct AttnSmem {
+  static constexpr int KP = D + 8;          // K row pitch (bf16)
+  static constexpr int VP = kBK + 8;        // V^T row pitch (bf16)
+  uint16_t ks[kBK * KP];
+  uint16_t vt[D * VP];
+  float bias[4][kBK];
+};
+
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+template <int D, int HPW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
+__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const float* __restrict__ key_score,
+    const float* __restrict__ gain, const float* __restrict__ q_scale, float scale_log2,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
+    int32_t n_pblocks, int32_t n_hgroups) {
+  constexpr int PB = 32 * (4 / HPW);        // query positions per workgroup
+  constexpr int DK = D / 16;                // k-steps of S^T = K Q^T
+  constexpr int DB = D / 32;                // 32-row blocks of O^T
+  constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
+  constexpr int KRPI = 256 / CPR;           // K rows staged per pass
+  constexpr int KI = kBK / KRPI;            // K staging passes
+  constexpr int VT = (kBK / 4) * CPR;       // threads that stage V
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;                 // which half of the wave
+
+  const int hg = blockIdx.x % n_hgroups;
+  const int prank = blockIdx.x / n_hgroups;
+  const int pblock = CAUSAL ? n_pblocks - 1 - prank : prank;
+  const int G = Hq / Hkv;
+  const int head = hg * HPW + (wave % HPW);
+  const int kvh = (hg * HPW) / G;
+  const int pos0 = pblock * PB + 32 * (wave / HPW);
+  const int my_q = pos0 + l32;
+  const bool q_ok = my_q < N;
+
+  const int64_t q_stride = static_cast<int64_t>(Hq) * D;
+  const int64_t kv_stride = static_cast<int64_t>(Hkv) * D;
+
+  // Q^T as B operand: lane (query l32, half hh) holds d = 16 ks + 8 hh .. +7
+  bf16x8 qf[DK];
+  {
+    const uint16_t* qp = q + static_cast<int64_t>(q_ok ? my_q : 0) * q_stride +
+                         static_cast<int64_t>(head) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks)
+      qf[ks] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks) : bf16x8{};
+  }
+  const float cr = HAS_QSCALE ? (q_ok ? q_scale[my_q] : 1.0f) : 1.0f;
+
+  const int wg_end = CAUSAL ? min((pblock + 1) * PB, N) : N;
+  const int n_tiles = (wg_end + kBK - 1) / kBK;
+
+  // ---- staging roles ------------------------------------------------------
+  const int krow = tid / CPR, kchunk = tid % CPR;          // K: row-major copy
+  const int vkg = tid % (kBK / 4), vdc = tid / (kBK / 4);  // V: 4 keys x 8 dims
+  u32x4 kr[KI], vr[4];
+  auto load_tile = [&](int t) {
+    const int k0 = t * kBK;
+#pragma unroll
+    for (int i = 0; i < KI; ++i) {
+      const int key = k0 + krow + KRPI * i;
+      kr[i] = key < N ? *reinterpret_cast<const u32x4*>(
+                            k + static_cast<int64_t>(key) * kv_stride +
+                            static_cast<int64_t>(kvh) * D + 8 * kchunk)
+                      : u32x4{0, 0, 0, 0};
+    }
+    if (tid < VT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + 4 * vkg + j;
+        vr[j] = key < N ? *reinterpret_cast<const u32x4*>(
+                              v + static_cast<int64_t>(key) * kv_stride +
+                              static_cast<int64_t>(kvh) * D + 8 * vdc)
+                        : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  float bias_reg = 0.0f;  // this thread's staged bias entry
+  auto load_bias = [&](int t) {
+    if (HAS_BIAS && tid < HPW * kBK) {
+      const int key = t * kBK + (tid % kBK);
+      const int hw = tid / kBK;
+      bias_reg = key < N ? gain[hg * HPW + hw] * kLog2e * key_score[key] : 0.0f;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      *reinterpret_cast<u32x4*>(&sm.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kr[i];
+    if (tid < VT) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
+        u32x2 lo, hi;
+        lo[0] = pack_lo(vr[0][w], vr[1][w]);
+        lo[1] = pack_lo(vr[2][w], vr[3][w]);
+        hi[0] = pack_hi(vr[0][w], vr[1][w]);
+        hi[1] = pack_hi(vr[2][w], vr[3][w]);
+        *reinterpret_cast<u32x2*>(&sm.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + 4 * vkg]) = lo;
+        *reinterpret_cast<u32x2*>(&sm.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + 4 * vkg]) = hi;
+      }
+    }
+    if (HAS_BIAS && tid < HPW * kBK) sm.bias[tid / kBK][tid % kBK] = bias_reg;
+  };
+
+  // ---- running state --------------------------------------------------------
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
+  float m_run = -INFINITY;  // running max of y = scale*log2e*qk + bias (per query)
+  float l_run = 0.0f;       // this lane's share of the running sum
+
+  load_tile(0);
+  load_bias(0);
+  store_tile();
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * kBK;
+    const bool more = t + 1 < n_tiles;
+    if (more) {
+      load_tile(t + 1);
+      load_bias(t + 1);
+    }
+
+    // S^T = K Q^T for two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      const uint16_t* kp = &sm.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh];
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+
+    // logits in log2 units: y = scale*log2e*qk + gain*log2e*score
+    const bool need_mask = (CAUSAL && k0 + kBK - 1 > pos0) || (k0 + kBK > N);
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 b4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (HAS_BIAS)
+          b4 = *reinterpret_cast<const f32x4*>(&sm.bias[wave % HPW][32 * kb + 8 * j + 4 * hh]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * j + i;
+          float y = HAS_BIAS ? fmaf(s[kb][r], scale_log2, b4[i]) : s[kb][r] * scale_log2;
+          if (need_mask) {
+            const int key = k0 + 32 * kb + 8 * j + 4 * hh + i;
+            if (key >= N || (CAUSAL && key > my_q)) y = -INFINITY;
+          }
+          s[kb][r] = y;
+          tmax = fmaxf(tmax, y);
+        }
+      }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float cm = cr * m_use;
+    if (__any(m_new > m_run)) {
+      const float alpha = exp2f(cr * (m_run - m_use));  // 0 on the first visible tile
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+    }
+    m_run = m_new;
+
+    // P^T = exp2(c (y - m)) as bf16, already laid out as the PV B operand
+    bf16x8 p[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = exp2f(fmaf(cr, s[kb][8 * hf + i], -cm));
+          l_run += e;
+          p[kb][hf][i] = static_cast<__bf16>(e);
+        }
+      }
+    }
+
+    // O^T += V^T P^T: k-step (kb, hf) covers keys 32kb + 16hf + {4hh..4hh+3, 8+4hh..8+4hh+3}
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int kcol = 32 * kb + 16 * hf + 4 * hh;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint16_t* vp = &sm.vt[(32 * db + l32) * AttnSmem<D>::VP + kcol];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+          const u32x4 a4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
+                                                          p[kb][hf], o[db], 0, 0, 0);
+        }
+      }
+    }
+
+    __syncthreads();
+    if (more) {
+      store_tile();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  if (q_ok) {
+    uint16_t* op = out + static_cast<int64_t>(my_q) * q_stride + static_cast<int64_t>(head) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        bf16x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = static_cast<__bf16>(o[db][4 * j + i] * inv);
+        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
+      }
+    }
+    if (lse != nullptr && hh == 0) {
+      const float L = l_tot > 0.0f ? kLn2 * (cr * (m_run == -INFINITY ? 0.0f : m_run) + log2f(l_tot)) : -INFINITY;
+      lse[static_cast<int64_t>(head) * N + my_q] = L;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path: one thread per (query row, query head), online softmax in fp32.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(128) void attn_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const float* __restrict__ key_score, const float* __restrict__ gain,
+    const float* __restrict__ q_scale, float scale, int causal, float* __restrict__ out,
+    float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv) {
+  const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (idx >= static_cast<int64_t>(N) * Hq) return;
+  const int r = static_cast<int>(idx / Hq);
+  const int h = static_cast<int>(idx % Hq);
+  const int kvh = h / (Hq / Hkv);
+  const float c = q_scale ? q_scale[r] : 1.0f;
+  const float g = key_score ? gain[h] : 0.0f;
+  float qr[D], acc[D];
+  const float* qp = q + (static_cast<int64_t>(r) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) {
+    qr[e] = qp[e];
+    acc[e] = 0.0f;
+  }
+  float m = -INFINITY, l = 0.0f;
+  const int nk = causal ? r + 1 : N;
+  for (int j = 0; j < nk; ++j) {
+    const float* kp = k + (static_cast<int64_t>(j) * Hkv + kvh) * D;
+    float dot = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D; ++e) dot = fmaf(qr[e], kp[e], dot);
+    const float z = c * (scale * dot + (key_score ? g * key_score[j] : 0.0f));
+    if (z == -INFINITY) continue;
+    const float* vp = v + (static_cast<int64_t>(j) * Hkv + kvh) * D;
+    if (z > m) {
+      const float a = expf(m - z);
+      l = l * a + 1.0f;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(acc[e], a, vp[e]);
+      m = z;
+    } else {
+      const float w = expf(z - m);
+      l += w;
+#pragma unroll
+      for (int e = 0; e < D; ++e) acc[e] = fmaf(w, vp[e], acc[e]);
+    }
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  float* op = out + (static_cast<int64_t>(r) * Hq + h) * D;
+#pragma unroll
+  for (int e = 0; e < D; ++e) op[e] = acc[e] * inv;
+  if (lse) lse[static_cast<int64_t>(h) * N + r] = l > 0.0f ? m + logf(l) : -INFINITY;
+}
+
+template <int D, int HPW, bool CAUSAL>
+void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const float* ks, const float* gain, const float* qs, float scale_log2,
+                      uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
+                      int32_t npb, int32_t nhg) {
+#define TG_ATTN_LAUNCH(B, Q)                                                         \
+  attn_bf16_kernel<D, HPW, CAUSAL, B, Q><<<grid, dim3(256), 0, s>>>(                \
+      q, k, v, ks, gain, qs, scale_log2, out, lse, N, Hq, Hkv, npb, nhg)
+  if (has_bias) {
+    if (has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
+  } else {
+    if (has_qs) TG_ATTN_LAUNCH(false, true); else TG_ATTN_LAUNCH(false, false);
+  }
+#undef TG_ATTN_LAUNCH
+}
+
+template <int D, int HPW>
+void launch_bf16_attn_c(bool causal, bool has_bias, bool has_qs, int32_t N, int32_t Hq,
+                        int32_t Hkv, hipStream_t s, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, const float* ks, const float* gain,
+                        const float* qs, float scale_log2, uint16_t* out, float* lse) {
+  constexpr int PB = 32 * (4 / HPW);
+  const int32_t npb = (N + PB - 1) / PB;
+  const int32_t nhg = Hq / HPW;
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(npb) * nhg));
+  if (causal)
+    launch_bf16_attn<D, HPW, true>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
+                                   scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+  else
+    launch_bf16_attn<D, HPW, false>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
+                                    scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                                      int64_t D, const void* q, const void* k, const void* v,
+                                      const float* key_score, const float* gain,
+                                      const float* q_scale, float softmax_scale, int causal,
+                                      void* out, float* lse, void* stream) {
+  using namespace tg;
+  if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: unknown dtype %d", (int)dt);
+  if (N < 0 || N > kMaxTokens || Hq < 1 || Hkv < 1 || Hq > 65536 || Hkv > 65536)
+    return fail(TG_ERR_INVALID_ARGUMENT,
+                "tg_bias_attn_fwd: need 0 <= N <= 2^31-1 and 1 <= Hkv, Hq (N=%lld Hq=%lld Hkv=%lld)",
+                (long long)N, (long long)Hq, (long long)Hkv);
+  if (Hq % Hkv != 0)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: Hq %% Hkv != 0 (%lld, %lld)",
+                (long long)Hq, (long long)Hkv);
+  if (D != 64 && D != 128)
+    return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: head dim must be 64 or 128 (D=%lld)",
+                (long long)D);
+  if (N * Hq > kMaxTokens)
+    return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: N * Hq must fit in int32");
+  if (N == 0) {
+    clear_error();
+    return TG_OK;
+  }
+  if (!q || !k || !v || !out)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: NULL q/k/v/out");
+  if (key_score && !gain)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: key_score given without gain");
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16))
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: q/k/v/out must be 16-byte aligned");
+  const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(D));
+  hipStream_t s = as_stream(stream);
+  const int32_t n = static_cast<int32_t>(N), hq = static_cast<int32_t>(Hq),
+                hkv = static_cast<int32_t>(Hkv);
+  if (dt == TG_DTYPE_F32) {
+    const int64_t threads = N * Hq;
+    const dim3 grid(static_cast<uint32_t>((threads + 127) / 128));
+    if (D == 64)
+      attn_f32_kernel<64><<<grid, dim3(128), 0, s>>>(
+          static_cast<const float*>(q), static_cast<const float*>(k),
+          static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
+          static_cast<float*>(out), lse, n, hq, hkv);
+    else
+      attn_f32_kernel<128><<<grid, dim3(128), 0, s>>>(
+          static_cast<const float*>(q), static_cast<const float*>(k),
+          static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
+          static_cast<float*>(out), lse, n, hq, hkv);
+    return check_launch("tg_bias_attn_fwd");
+  }
+  const int64_t G = Hq / Hkv;
+  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const auto* qb = static_cast<const uint16_t*>(q);
+  const auto* kb = static_cast<const uint16_t*>(k);
+  const auto* vb = static_cast<const uint16_t*>(v);
+  auto* ob = static_cast<uint16_t*>(out);
+  const float sl2 = scale * kLog2e;
+  const bool cz = causal != 0, hb = key_score != nullptr, hs = q_scale != nullptr;
+#define TG_ATTN_DISPATCH(DD, HH) \
+  launch_bf16_attn_c<DD, HH>(cz, hb, hs, n, hq, hkv, s, qb, kb, vb, key_score, gain, q_scale, sl2, ob, lse)
+  if (D == 128) {
+    if (hpw == 4) TG_ATTN_DISPATCH(128, 4);
+    else if (hpw == 2) TG_ATTN_DISPATCH(128, 2);
+    else TG_ATTN_DISPATCH(128, 1);
+  } else {
+    if (hpw == 4) TG_ATTN_DISPATCH(64, 4);
+    else if (hpw == 2) TG_ATTN_DISPATCH(64, 2);
+    else TG_ATTN_DISPATCH(64, 1);
+  }
+#undef TG_ATTN_DISPATCH
+  return check_launch("tg_bias_attn_fwd");
+}

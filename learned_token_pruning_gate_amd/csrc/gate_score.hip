@@ -1,0 +1,345 @@
+// gate_score.hip -- [a1] the gate's scorer: RMSNorm of each prunable token's
+// residual row followed by an MLP d -> h (SiLU) -> 1.
+//
+// TokenGate pages: ai.info summary "Key Contributions" item 1 (a scoring MLP
+// over the RMSNorm-normalised post-attention residual scores the prunable
+// tokens), the techbycountry explainer "how the gate works" and the README
+// mirror "How it works".
+//
+// bf16 path (gfx950).  The gate reads every prunable residual row once
+// (n_P * d * 2 bytes) and performs 2 * n_P * d * h flops: at h = 256 that
+// is 256 flop per byte, just under the MI355X bf16 ridge, so the kernel is
+// built to stream the residual at HBM rate while the MFMA pipes keep up:
+//   * RMSNorm is folded into a per-row scale applied after the projection:
+//     W1 (gamma * x / rms) = (W1 (gamma * x)) / rms, so the row's sum of
+//     squares is accumulated from the same registers that stage the tile;
+//   * a workgroup owns TM rows and all h outputs; the TM x 64 residual tile
+//     of each k-stage goes HBM -> registers -> padded LDS (double buffered,
+//     one barrier per stage) and is read by the four waves as MFMA A
+//     operands;
+//   * each wave owns h/4 output columns and streams its slice of W1 (which
+//     stays resident in each XCD's L2) straight into registers as MFMA B
+//     operands, one stage ahead;
+//   * v_mfma_f32_16x16x32_bf16 accumulates z in fp32; the epilogue applies
+//     1/rms, b1, SiLU and w2 per element and reduces over h inside 16-lane
+//     rows and then across the four waves through LDS.
+//
+// f32 path: one wave per row on the vector ALUs (fp32 throughout).
+#include "tg_common.hpp"
+
+namespace tg {
+namespace {
+
+constexpr int kKS = 64;                 // k elements per stage
+constexpr int kPitch = kKS + 8;         // LDS row pitch in bf16 (144 bytes)
+
+template <int TM, int NT, bool HAS_GAMMA>
+__global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
+    const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
+    const float* __restrict__ gamma, float eps, const uint16_t* __restrict__ w1,
+    const float* __restrict__ b1, const float* __restrict__ w2, float b2,
+    float* __restrict__ scores, int32_t T, int32_t d) {
+  constexpr int RPT = TM / 32;          // staged rows per thread
+  constexpr int MT = TM / 16;           // 16-row MFMA tiles per wave
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kPitch];
+  __shared__ float s_rs[TM];
+  __shared__ float s_part[4][TM];
+  __shared__ int s_any;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * TM;
+
+  // staging role: row (tid/8) + 32 i, 16-byte chunk tid % 8 of the stage
+  const int chunk = tid & 7;
+  bool live[RPT];
+  const uint16_t* xrow[RPT];
+  int any = 0;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int64_t r = row0 + (tid >> 3) + 32 * i;
+    live[i] = (r < T) && prunable[r] != 0;
+    any |= live[i];
+    xrow[i] = resid + (live[i] ? r : 0) * ld_x + chunk * 8;
+  }
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  if (any) s_any = 1;
+  __syncthreads();
+  if (!s_any) {  // no prunable row in this tile
+    if (tid < TM && row0 + tid < T) scores[row0 + tid] = 0.0f;
+    return;
+  }
+
+  // compute role: wave owns columns [wave*16*NT, (wave+1)*16*NT)
+  const int hbase = wave * 16 * NT;
+  const int lrow = lane & 15;            // A row / B column inside a 16x16 tile
+  const int lk = (lane >> 4) * 8;        // k offset of this lane's 8 elements
+  const uint16_t* wrow[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wrow[nt] = w1 + static_cast<int64_t>(hbase + nt * 16 + lrow) * d + lk;
+
+  const int nstages = (d + kKS - 1) / kKS;
+  float ss[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) ss[i] = 0.0f;
+
+  u32x4 xr[RPT];
+  auto load_x = [&](int s) {
+    const int k = s * kKS + chunk * 8;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (live[i] && k < d)
+        xr[i] = *reinterpret_cast<const u32x4*>(xrow[i] + s * kKS);
+      else
+        xr[i] = u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_x = [&](int s, int buf) {
+    const int k = s * kKS + chunk * 8;
+    float g[8];
+    if (HAS_GAMMA) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) g[e] = (k + e < d) ? gamma[k + e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      u32x4 v = xr[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(v[e] << 16);
+        const float hi = __uint_as_float(v[e] & 0xffff0000u);
+        ss[i] = fmaf(lo, lo, ss[i]);
+        ss[i] = fmaf(hi, hi, ss[i]);
+        if (HAS_GAMMA) {
+          __bf16 blo = static_cast<__bf16>(lo * g[2 * e]);
+          __bf16 bhi = static_cast<__bf16>(hi * g[2 * e + 1]);
+          v[e] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, blo)) |
+                 (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, bhi)) << 16);
+        }
+      }
+      const int r = (tid >> 3) + 32 * i;
+      *reinterpret_cast<u32x4*>(&xs[buf][r * kPitch + chunk * 8]) = v;
+    }
+  };
+
+  bf16x8 wc[NT][2], wn[NT][2];
+  auto load_w = [&](int s, bf16x8 (&w)[NT][2]) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int k = s * kKS + kk * 32 + lk;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        if (k < d)
+          w[nt][kk] = *reinterpret_cast<const bf16x8*>(wrow[nt] + s * kKS + kk * 32);
+        else
+          w[nt][kk] = bf16x8{};
+      }
+    }
+  };
+
+  f32x4 acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load_x(0);
+  load_w(0, wc);
+  store_x(0, 0);
+  __syncthreads();
+
+  for (int s = 0; s < nstages; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nstages;
+    if (more) {
+      load_x(s + 1);
+      load_w(s + 1, wn);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8*>(&xs[buf][(mt * 16 + lrow) * kPitch + kk * 32 + lk]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wc[nt][kk], acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (more) store_x(s + 1, buf ^ 1);
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        wc[nt][0] = wn[nt][0];
+        wc[nt][1] = wn[nt][1];
+      }
+    }
+  }
+
+  // per-row 1/rms: reduce the sum of squares over the 8 lanes of a row
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    float v = ss[i];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    if (chunk == 0) s_rs[(tid >> 3) + 32 * i] = 1.0f / sqrtf(v / static_cast<float>(d) + eps);
+  }
+  __syncthreads();
+
+  // epilogue: z = acc/rms + b1; partial score over this wave's columns
+  float part[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[mt][r] = 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = hbase + nt * 16 + lrow;
+    const float bb = b1 ? b1[n] : 0.0f;
+    const float ww = w2[n];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tok = mt * 16 + (lane >> 4) * 4 + r;
+        const float z = fmaf(acc[mt][nt][r], s_rs[tok], bb);
+        part[mt][r] = fmaf(ww, z / (1.0f + expf(-z)), part[mt][r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = part[mt][r];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      v += __shfl_xor(v, 8, 64);
+      if (lrow == 0) s_part[wave][mt * 16 + (lane >> 4) * 4 + r] = v;
+    }
+  }
+  __syncthreads();
+  if (tid < TM) {
+    const int64_t t = row0 + tid;
+    if (t < T) {
+      const float s = b2 + ((s_part[0][tid] + s_part[1][tid]) + (s_part[2][tid] + s_part[3][tid]));
+      scores[t] = prunable[t] ? s : 0.0f;
+    }
+  }
+}
+
+// fp32 path: one wave per row.  u = gamma*x/rms is formed on the fly;
+// lane j accumulates z_j over the row (x broadcast from L1), then the wave
+// reduces w2 . SiLU(z) across lanes.
+__global__ __launch_bounds__(256) void gate_f32_kernel(
+    const float* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
+    const float* __restrict__ gamma, float eps, const float* __restrict__ w1,
+    const float* __restrict__ b1, const float* __restrict__ w2, float b2,
+    float* __restrict__ scores, int32_t T, int32_t d, int32_t h) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  if (!prunable[t]) {
+    if (lane == 0) scores[t] = 0.0f;
+    return;
+  }
+  const float* x = resid + t * ld_x;
+  float ss = 0.0f;
+  for (int i = lane; i < d; i += 64) ss = fmaf(x[i], x[i], ss);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  const float inv_rms = 1.0f / sqrtf(ss / static_cast<float>(d) + eps);
+  float part = 0.0f;
+  for (int j = lane; j < h; j += 64) {
+    const float* wr = w1 + static_cast<int64_t>(j) * d;
+    float z = 0.0f;
+    for (int i = 0; i < d; ++i) {
+      const float u = gamma ? gamma[i] * (x[i] * inv_rms) : x[i] * inv_rms;
+      z = fmaf(wr[i], u, z);
+    }
+    if (b1) z += b1[j];
+    part = fmaf(w2[j], z / (1.0f + expf(-z)), part);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+  if (lane == 0) scores[t] = b2 + part;
+}
+
+template <int TM, int NT>
+void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint16_t* x,
+                 int64_t ld, const uint8_t* p, const float* g, float eps, const uint16_t* w1,
+                 const float* b1, const float* w2, float b2, float* out, int32_t d) {
+  if (has_gamma)
+    gate_bf16_kernel<TM, NT, true><<<grid, dim3(256), 0, s>>>(
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+  else
+    gate_bf16_kernel<TM, NT, false><<<grid, dim3(256), 0, s>>>(
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                                   const void* resid, int64_t resid_row_stride,
+                                   const uint8_t* prunable, const float* rms_weight, float eps,
+                                   const void* w1, const float* b1, const float* w2, float b2,
+                                   float* scores, void* stream) {
+  using namespace tg;
+  if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: unknown dtype %d", (int)dt);
+  if (T < 0 || T > kMaxTokens || d < 1 || h < 1 || d > kMaxTokens || h > kMaxTokens)
+    return fail(TG_ERR_INVALID_ARGUMENT,
+                "tg_gate_score: need 0 <= T <= 2^31-1, d >= 1, h >= 1 (T=%lld d=%lld h=%lld)",
+                (long long)T, (long long)d, (long long)h);
+  if (!(eps >= 0.0f))
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: eps must be >= 0");
+  if (T == 0) {
+    clear_error();
+    return TG_OK;
+  }
+  if (!resid || !prunable || !w1 || !w2 || !scores)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: NULL resid/prunable/w1/w2/scores");
+  if (resid_row_stride < d)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: resid_row_stride %lld < d %lld",
+                (long long)resid_row_stride, (long long)d);
+  hipStream_t s = as_stream(stream);
+  if (dt == TG_DTYPE_F32) {
+    if (!aligned(resid, 4) || !aligned(w1, 4))
+      return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: misaligned f32 pointer");
+    const int64_t blocks = (T + 3) / 4;
+    gate_f32_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
+        static_cast<const float*>(resid), resid_row_stride, prunable, rms_weight, eps,
+        static_cast<const float*>(w1), b1, w2, b2, scores, static_cast<int32_t>(T),
+        static_cast<int32_t>(d), static_cast<int32_t>(h));
+    return check_launch("tg_gate_score");
+  }
+  if (d % 8 != 0)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gate_score: bf16 path needs d %% 8 == 0 (d=%lld)",
+                (long long)d);
+  if (h % 64 != 0 || h > 256)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_gate_score: bf16 path needs h in {64, 128, 192, 256} (h=%lld)",
+                (long long)h);
+  if (!aligned(resid, 16) || !aligned(w1, 16) || (resid_row_stride % 8) != 0)
+    return fail(TG_ERR_INVALID_ARGUMENT,
+                "tg_gate_score: bf16 resid/w1 must be 16-byte aligned, row stride %% 8 == 0");
+  const auto* x = static_cast<const uint16_t*>(resid);
+  const auto* w = static_cast<const uint16_t*>(w1);
+  const int32_t d32 = static_cast<int32_t>(d);
+  const bool g = rms_weight != nullptr;
+  constexpr int TM = 64;
+  const dim3 grid(static_cast<uint32_t>((T + TM - 1) / TM));
+  switch (h / 64) {
+    case 1: launch_bf16<TM, 1>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
+    case 2: launch_bf16<TM, 2>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
+    case 3: launch_bf16<TM, 3>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
+    default: launch_bf16<TM, 4>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
+  }
+  return check_launch("tg_gate_score");
+}

