@@ -1,0 +1,291 @@
+"""Benchmark of the token-gated prefill path on one MI355X.
+
+One step = the whole path over one prompt: gate scoring of T tokens, top-K
+selection + compaction, gather of the kept rows, and token-gated attention
+over the N kept tokens (one gate plus one upper attention layer).  Inputs
+are seeded synthetic tensors of the workload's shapes, resident in HBM
+before the timed region; outputs are preallocated.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t16k]
+
+Prints one JSON line: tokens/s for the whole step, per-stage event timings,
+the roofline of the dominant kernel, and the CPU oracle timed on a bounded
+sample of the same workload (a reported baseline, not the target).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "token-gated prefill tokens/s (score+topK+gather+bias attn); attn TFLOP/s vs peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+
+KERNEL_SOURCES = {
+    "gate": "gate_score.hip", "select": "topk_select.hip",
+    "gather": "compact_gather.hip", "attn": "bias_attn.hip",
+}
+
+
+def source_sha(stage: str) -> str:
+    p = os.path.join(ROOT, "learned_token_pruning_gate_amd", "csrc", KERNEL_SOURCES[stage])
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic(w, N):
+    """Per-launch algorithmic bytes and flops of each stage (what the method
+    must move or compute, not what a kernel happens to touch)."""
+    b = 2 if w.dtype == "bf16" else 4
+    nP, T, d, h = w.n_prunable, w.T, w.d, w.h
+    D, Hq, Hkv = w.D, w.Hq, w.Hkv
+    return {
+        "gate": dict(bytes=nP * d * b + T + 4 * T + h * d * b, flops=2 * nP * d * h),
+        "select": dict(bytes=4 * nP + T + 4 * N, flops=0),
+        "gather": dict(bytes=2 * N * d * b + 16 * N, flops=0),
+        "attn": dict(bytes=(2 * Hq + 2 * Hkv) * N * D * b + 8 * N,
+                     flops=2 * D * Hq * N * (N + 1)),
+    }
+
+
+def load_traffic(stage):
+    """HBM bytes per launch measured by rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a copy-kernel calibration), if recorded for the
+    current kernel source; None otherwise."""
+    p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(stage)
+    if not rec or rec.get("source_sha") != source_sha(stage):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, g, a, N, kept, scores_gpu, key_score):
+    """The oracle, as it stands, on a bounded sample of the same workload,
+    scaled to tokens/s of the whole step."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    T = w.T
+    pr = np.nonzero(g.prunable)[0]
+    n_gate = min(1024, len(pr))
+    gate_rows = pr[np.linspace(0, len(pr) - 1, n_gate).astype(np.int64)]
+    t0 = time.perf_counter()
+    oracle.gate_score(workloads.as_f64(g.resid[gate_rows], w.dtype), g.prunable[gate_rows],
+                      workloads.as_f64(g.w1, w.dtype), g.w2, b2=g.b2, gamma=g.gamma, b1=g.b1,
+                      eps=g.eps)
+    t_gate = (time.perf_counter() - t0) * len(pr) / n_gate
+    t0 = time.perf_counter()
+    oracle.topk_select(scores_gpu, g.prunable, w.K)
+    t_sel = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.compact_gather(g.resid, scores_gpu, kept)
+    t_gat = time.perf_counter() - t0
+    n_rows = min(64, N)
+    rows = np.linspace(0, N - 1, n_rows).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.bias_attn(workloads.as_f64(a.q, w.dtype), workloads.as_f64(a.k, w.dtype),
+                     workloads.as_f64(a.v, w.dtype), key_score, a.gain, rows=rows)
+    t_att_sample = time.perf_counter() - t0
+    # causal work of row r is proportional to r + 1
+    t_att = t_att_sample * (N * (N + 1) / 2) / float(np.sum(rows + 1))
+    total = t_gate + t_sel + t_gat + t_att
+    sample_s = t_gate * n_gate / len(pr) + t_sel + t_gat + t_att_sample
+    return {
+        "value": T / total, "unit": "tokens/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": ("fp64 C oracle on this host: gate on %d of %d prunable rows, full top-K "
+                   "and gather, attention on %d of %d query rows (all heads); each stage "
+                   "scaled to the full step by its row count (attention by causal work); "
+                   "%.1f s of CPU work" % (n_gate, len(pr), n_rows, N, sample_s)),
+        "stage_seconds_est": {"gate": t_gate, "select": t_sel, "gather": t_gat,
+                              "attn": t_att},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="t16k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps with the last-level cache flushed before each")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the path runs on one "
+              "MI355X; multi-GPU sharding is a design note, not built); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import learned_token_pruning_gate_amd as tg
+    import workloads
+
+    w = workloads.get(args.workload)
+    g, a = workloads.generate(w)
+    N = w.n_kept
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def up(x, dt=None):
+        x = np.ascontiguousarray(x)
+        if dt == "bf16":
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(x).to(dev)
+
+    dt = w.dtype
+    resid, prunable = up(g.resid, dt), up(g.prunable)
+    w1, w2, b1, gamma = up(g.w1, dt), up(g.w2), up(g.b1), up(g.gamma)
+    q, k, v, gain = up(a.q, dt), up(a.k, dt), up(a.v, dt), up(a.gain)
+    scores = torch.empty(w.T, dtype=torch.float32, device=dev)
+    kept = torch.empty(w.T, dtype=torch.int32, device=dev)
+    n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    ws = torch.zeros(tg.tg_topk_workspace_size(w.T), dtype=torch.uint8, device=dev)
+    resid_kept = torch.empty((N, w.d), dtype=resid.dtype, device=dev)
+    pos_kept = torch.empty(N, dtype=torch.int32, device=dev)
+    score_kept = torch.empty(N, dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((w.Hq, N), dtype=torch.float32, device=dev)
+    drawn = up(a.drawn_scores) if w.drawn_key_scores else None
+    q_scale = None
+    if w.q_scale_recipe == "pos_rank":
+        kept_host = np.sort(np.concatenate([np.nonzero(g.prunable == 0)[0],
+                                            np.nonzero(g.prunable)[0][: w.K]]))
+        q_scale = up(workloads.q_scale_pos_rank(kept_host)) if w.K >= w.n_prunable else None
+
+    # Prepared C calls: argument marshalling done once, outside the timed loop.
+    lib = tg.load()
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    dtc = tg.TG_DTYPE_BF16 if dt == "bf16" else tg.TG_DTYPE_F32
+    key_ptr = P(drawn) if drawn is not None else P(score_kept)
+    F = ctypes.c_float
+    gate_args = (dtc, w.T, w.d, w.h, P(resid), resid.stride(0), P(prunable), P(gamma),
+                 F(g.eps), P(w1), P(b1), P(w2), F(g.b2), P(scores), sp)
+    sel_args = (w.T, P(scores), P(prunable), w.K, P(kept), kept.numel(), P(n_kept), P(ws),
+                ws.numel(), sp)
+    gat_args = (dtc, w.T, N, w.d, P(resid), resid.stride(0), P(scores), P(kept),
+                P(resid_kept), resid_kept.stride(0), P(pos_kept), P(score_kept), sp)
+    att_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), key_ptr, P(gain), P(q_scale),
+                F(0.0), 1, P(out), P(lse), sp)
+
+    def check(st, name):
+        if st != 0:
+            raise RuntimeError("%s failed: %s %s" % (name, tg.tg_status_str(st),
+                                                     tg.tg_last_error()))
+
+    stages = ["gate", "select", "gather", "attn"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        check(lib.tg_gate_score(*gate_args), "tg_gate_score")
+        if ev is not None:
+            ev[1].record(stream)
+        check(lib.tg_topk_select(*sel_args), "tg_topk_select")
+        if ev is not None:
+            ev[2].record(stream)
+        check(lib.tg_compact_gather(*gat_args), "tg_compact_gather")
+        if ev is not None:
+            ev[3].record(stream)
+        check(lib.tg_bias_attn_fwd(*att_args), "tg_bias_attn_fwd")
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    per_stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
+                    for j, s in enumerate(stages)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = w.T * args.steps / elapsed
+
+    alg = algorithmic(w, N)
+    stage_info = {}
+    for s in stages:
+        t = per_stage_ms[s] * 1e-3
+        info = {"ms": per_stage_ms[s], "bytes": alg[s]["bytes"],
+                "GB_s": alg[s]["bytes"] / t / 1e9,
+                "hbm_frac": alg[s]["bytes"] / t / 1e9 / PEAK_HBM_GBS}
+        if alg[s]["flops"]:
+            peak = PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS
+            info["TFLOP_s"] = alg[s]["flops"] / t / 1e12
+            info["mfma_frac"] = info["TFLOP_s"] / peak
+        stage_info[s] = info
+    dominant = max(stages, key=lambda s: per_stage_ms[s])
+    di = stage_info[dominant]
+    if dominant == "attn" or (dominant == "gate" and di.get("mfma_frac", 0) > di["hbm_frac"]):
+        roof = {"bound": "mfma", "achieved": di["TFLOP_s"],
+                "peak": PEAK_BF16_TFLOPS if dt == "bf16" else PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s", "frac": di["mfma_frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": di["GB_s"], "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": di["hbm_frac"]}
+    roof["kernel"] = dominant
+    roof["traffic"] = load_traffic(dominant)
+
+    cold = None
+    if args.cold:
+        flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)  # 512 MiB > MALL
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+        for e in ev:
+            flush.fill_(1)
+            step(e)
+        torch.cuda.synchronize()
+        cold = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in ev]))
+                for j, s in enumerate(stages)}
+        del flush
+
+    result = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "d": w.d, "h": w.h,
+                   "n_prunable": w.n_prunable, "K": w.K, "N_kept": N, "Hq": w.Hq,
+                   "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
+                   "parallelism": "single-gpu"},
+        "attn_tflops": stage_info["attn"].get("TFLOP_s"),
+        "attn_frac_of_peak": stage_info["attn"].get("mfma_frac"),
+        "roofline": roof,
+        "stages": stage_info,
+    }
+    if cold:
+        result["cold_stage_ms"] = cold
+
+    if not args.no_cpu_baseline:
+        kept_host = kept.cpu().numpy()[:N]
+        key_host = (drawn if drawn is not None else score_kept).cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, g, a, N, kept_host, scores.cpu().numpy(),
+                                              key_host)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
