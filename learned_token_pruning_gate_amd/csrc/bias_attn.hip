@@ -50,9 +50,9 @@ template <int D>
 struct AttnSmem {
   static constexpr int KP = D + 8;          // K row pitch (bf16)
   static constexpr int VP = kBK + 8;        // V^T row pitch (bf16)
-  uint16_t ks[kBK * KP];
-  uint16_t vt[D * VP];
-  float bias[4][kBK];
+  uint16_t ks[kBK * KP];                    // K tile, row-major [key][dim]
+  uint16_t vt[D * VP];                      // V tile transposed [dim][key]
+  u32x2 bias[4][kBK];                       // per head: bf16 (hi | mid << 16, lo)
 };
 
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
@@ -61,22 +61,43 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return (a >> 16) | (b & 0xffff0000u);
 }
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ __forceinline__ float bf16_val(uint32_t bits) {
+  return __uint_as_float(bits << 16);
+}
+
+// Logits are tracked in log2 units, y = log2(e) * z.  A tile maximum below
+// kMaskedLog2 counts as "no visible key" (a -inf score is encoded as a bias
+// far below it).
+constexpr float kMaskedLog2 = -524288.0f;
+
+// The bias enters the MFMA as three bf16 terms hi + mid + lo, which carry a
+// fp32 value to within 2^-25 of itself: (hi | mid << 16, lo).
+__device__ __forceinline__ u32x2 split_bf16_triple(float v) {
+  const uint32_t hi = bf16_bits(v);
+  const float r1 = v - bf16_val(hi);
+  const uint32_t mid = bf16_bits(r1);
+  const uint32_t lo = bf16_bits(r1 - bf16_val(mid));
+  return u32x2{hi | (mid << 16), lo};
+}
 
 template <int D, int HPW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
-    const float* __restrict__ gain, const float* __restrict__ q_scale, float scale_log2,
+    const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
     int32_t n_pblocks, int32_t n_hgroups) {
   constexpr int PB = 32 * (4 / HPW);        // query positions per workgroup
-  constexpr int DK = D / 16;                // k-steps of S^T = K Q^T
+  constexpr int DK = D / 16;                // k-steps of S^T = K Q^T (plus one extra)
   constexpr int DB = D / 32;                // 32-row blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
   constexpr int KRPI = 256 / CPR;           // K rows staged per pass
   constexpr int KI = kBK / KRPI;            // K staging passes
   constexpr int VT = (kBK / 4) * CPR;       // threads that stage V
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm;
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -88,80 +109,96 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   const int prank = blockIdx.x / n_hgroups;
   const int pblock = CAUSAL ? n_pblocks - 1 - prank : prank;
   const int G = Hq / Hkv;
-  const int head = hg * HPW + (wave % HPW);
+  const int hw = wave % HPW;
+  const int head = hg * HPW + hw;
   const int kvh = (hg * HPW) / G;
   const int pos0 = pblock * PB + 32 * (wave / HPW);
   const int my_q = pos0 + l32;
   const bool q_ok = my_q < N;
 
-  const int64_t q_stride = static_cast<int64_t>(Hq) * D;
-  const int64_t kv_stride = static_cast<int64_t>(Hkv) * D;
+  const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;     // bytes per token
+  const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
+  const __amdgpu_buffer_rsrc_t q_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(q), 0, static_cast<int>(static_cast<uint32_t>(N) * q_row), 0x00020000);
+  const __amdgpu_buffer_rsrc_t k_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(v), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
 
-  // Q^T as B operand: lane (query l32, half hh) holds d = 16 ks + 8 hh .. +7
-  bf16x8 qf[DK];
+  // y = ac * (<q, k> + bias'_k), with ac = scale * log2(e) * c_r and the
+  // per-key bias'_k = gain * score_k / scale in dot-product units.
+  const float cr = HAS_QSCALE ? (q_ok ? q_scale[my_q] : 1.0f) : 1.0f;
+  const float ac = scale * kLog2e * cr;
+
+  // Q^T as MFMA B operand (exact bf16): lane (query l32, half hh) holds dims
+  // 16 ks + 8 hh .. +7.  k-step DK is the extra one: [1, 1, 1, 0...] in the
+  // hh = 0 half, matched on the key side by [bias'_hi, bias'_mid, bias'_lo,
+  // 0...], so the MFMA adds the gate bias to every logit.
+  bf16x8 qf[DK + 1];
   {
-    const uint16_t* qp = q + static_cast<int64_t>(q_ok ? my_q : 0) * q_stride +
-                         static_cast<int64_t>(head) * D + 8 * hh;
+    const uint32_t base = static_cast<uint32_t>(my_q) * q_row +
+                          static_cast<uint32_t>(head) * D * 2 + 16u * hh;
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks)
-      qf[ks] = q_ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * ks) : bf16x8{};
+      qf[ks] = __builtin_bit_cast(bf16x8,
+                                  __builtin_amdgcn_raw_buffer_load_b128(q_rs, base + 32u * ks, 0, 0));
   }
-  const float cr = HAS_QSCALE ? (q_ok ? q_scale[my_q] : 1.0f) : 1.0f;
+  qf[DK] = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
+                                              : u32x4{0, 0, 0, 0});
+  float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
 
   const int wg_end = CAUSAL ? min((pblock + 1) * PB, N) : N;
   const int n_tiles = (wg_end + kBK - 1) / kBK;
+  const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
 
   // ---- staging roles ------------------------------------------------------
   const int krow = tid / CPR, kchunk = tid % CPR;          // K: row-major copy
   const int vkg = tid % (kBK / 4), vdc = tid / (kBK / 4);  // V: 4 keys x 8 dims
-  u32x4 kr[KI], vr[4];
+  const float inv_scale = 1.0f / scale;
+  // A -inf score becomes a bias of -2^21 log2 units (in dot-product units):
+  // for any per-query scale >= 0.25 the logit falls below kMaskedLog2 and its
+  // weight underflows to exactly 0, as deleting the key would give.
+  const float masked_bias = -2097152.0f * inv_scale / kLog2e;
+  u32x4 kreg[KI], vreg[4];
+  u32x2 breg = u32x2{0, 0};
   auto load_tile = [&](int t) {
     const int k0 = t * kBK;
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int key = k0 + krow + KRPI * i;
-      kr[i] = key < N ? *reinterpret_cast<const u32x4*>(
-                            k + static_cast<int64_t>(key) * kv_stride +
-                            static_cast<int64_t>(kvh) * D + 8 * kchunk)
-                      : u32x4{0, 0, 0, 0};
-    }
-    if (tid < VT) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + 4 * vkg + j;
-        vr[j] = key < N ? *reinterpret_cast<const u32x4*>(
-                              v + static_cast<int64_t>(key) * kv_stride +
-                              static_cast<int64_t>(kvh) * D + 8 * vdc)
-                        : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  float bias_reg = 0.0f;  // this thread's staged bias entry
-  auto load_bias = [&](int t) {
-    if (HAS_BIAS && tid < HPW * kBK) {
-      const int key = t * kBK + (tid % kBK);
-      const int hw = tid / kBK;
-      bias_reg = key < N ? gain[hg * HPW + hw] * kLog2e * key_score[key] : 0.0f;
-    }
-  };
-  auto store_tile = [&]() {
+    const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
 #pragma unroll
     for (int i = 0; i < KI; ++i)
-      *reinterpret_cast<u32x4*>(&sm.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kr[i];
+      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          k_rs, static_cast<uint32_t>(k0 + krow + KRPI * i) * kv_row + hoff + 16u * kchunk, 0, 0);
+    if (tid < VT) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(
+            v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
+    }
+    if (HAS_BIAS && tid < HPW * kBK) {
+      const int key = k0 + (tid % kBK);
+      const float sc = key < N ? key_score[key] : 0.0f;
+      breg = split_bf16_triple(sc == -INFINITY ? masked_bias
+                                               : gain[hg * HPW + tid / kBK] * sc * inv_scale);
+    }
+  };
+  auto store_tile = [&](AttnSmem<D>& b) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+      *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kreg[i];
     if (tid < VT) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
         u32x2 lo, hi;
-        lo[0] = pack_lo(vr[0][w], vr[1][w]);
-        lo[1] = pack_lo(vr[2][w], vr[3][w]);
-        hi[0] = pack_hi(vr[0][w], vr[1][w]);
-        hi[1] = pack_hi(vr[2][w], vr[3][w]);
-        *reinterpret_cast<u32x2*>(&sm.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + 4 * vkg]) = lo;
-        *reinterpret_cast<u32x2*>(&sm.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + 4 * vkg]) = hi;
+        lo[0] = pack_lo(vreg[0][w], vreg[1][w]);
+        lo[1] = pack_lo(vreg[2][w], vreg[3][w]);
+        hi[0] = pack_hi(vreg[0][w], vreg[1][w]);
+        hi[1] = pack_hi(vreg[2][w], vreg[3][w]);
+        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + 4 * vkg]) = lo;
+        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + 4 * vkg]) = hi;
       }
     }
-    if (HAS_BIAS && tid < HPW * kBK) sm.bias[tid / kBK][tid % kBK] = bias_reg;
+    if (HAS_BIAS && tid < HPW * kBK) b.bias[tid / kBK][tid % kBK] = breg;
   };
 
   // ---- running state --------------------------------------------------------
@@ -170,65 +207,69 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
-  float m_run = -INFINITY;  // running max of y = scale*log2e*qk + bias (per query)
-  float l_run = 0.0f;       // this lane's share of the running sum
+  float l_run = 0.0f;       // this lane's share of the running sum of 2^y
 
   load_tile(0);
-  load_bias(0);
-  store_tile();
+  store_tile(sm[0]);
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
+    const AttnSmem<D>& b = sm[t & 1];
     const int k0 = t * kBK;
     const bool more = t + 1 < n_tiles;
-    if (more) {
-      load_tile(t + 1);
-      load_bias(t + 1);
-    }
+    if (more) load_tile(t + 1);
 
-    // S^T = K Q^T for two 32-key blocks
+    // S'^T = K' Q'^T = <q, k> + bias'
     f32x16 s[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      const uint16_t* kp = &sm.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh];
+      const uint16_t* kp = &b.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh];
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
+      u32x4 ke = u32x4{0, 0, 0, 0};
+      if (hh == 0) {
+        const u32x2 bb = HAS_BIAS ? b.bias[hw][32 * kb + l32] : u32x2{0, 0};
+        ke[0] = bb[0];                     // [bias'_hi, bias'_mid]
+        ke[1] = bb[1];                     // [bias'_lo, 0]
+      }
+      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ke), qf[DK],
+                                                      s[kb], 0, 0, 0);
     }
 
-    // logits in log2 units: y = scale*log2e*qk + gain*log2e*score
+    // causal / tail mask (only tiles that reach past a query or past N)
     const bool need_mask = (CAUSAL && k0 + kBK - 1 > pos0) || (k0 + kBK > N);
+    if (need_mask) {
+      const int rel = lim - k0 - 4 * hh;   // key index k0 + 4hh + c is visible iff c <= rel
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = c <= rel ? s[kb][r] : -INFINITY;
+        }
+    }
+
     float tmax = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        f32x4 b4 = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (HAS_BIAS)
-          b4 = *reinterpret_cast<const f32x4*>(&sm.bias[wave % HPW][32 * kb + 8 * j + 4 * hh]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          float y = HAS_BIAS ? fmaf(s[kb][r], scale_log2, b4[i]) : s[kb][r] * scale_log2;
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * j + 4 * hh + i;
-            if (key >= N || (CAUSAL && key > my_q)) y = -INFINITY;
-          }
-          s[kb][r] = y;
-          tmax = fmaxf(tmax, y);
-        }
-      }
-    }
+      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
+
+    // running max in log2 units (ac > 0 keeps the arg-max); maxima below
+    // kMaskedLog2 are masked keys only
+    float tm = tmax * ac;
+    tm = tm > kMaskedLog2 ? tm : -INFINITY;
+    const float m_new = fmaxf(m_run, tm);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float cm = cr * m_use;
     if (__any(m_new > m_run)) {
-      const float alpha = exp2f(cr * (m_run - m_use));  // 0 on the first visible tile
+      // 0 when nothing was accumulated yet
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -237,20 +278,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     }
     m_run = m_new;
 
-    // P^T = exp2(c (y - m)) as bf16, already laid out as the PV B operand
+    // P^T = 2^(y - m) as bf16, already laid out as the PV B operand; the row
+    // maximum gets weight exactly 1
     bf16x8 p[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float e = exp2f(fmaf(cr, s[kb][8 * hf + i], -cm));
+          const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + i], ac, -m_use));
           l_run += e;
           p[kb][hf][i] = static_cast<__bf16>(e);
         }
-      }
-    }
 
     // O^T += V^T P^T: k-step (kb, hf) covers keys 32kb + 16hf + {4hh..4hh+3, 8+4hh..8+4hh+3}
 #pragma unroll
@@ -260,7 +300,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         const int kcol = 32 * kb + 16 * hf + 4 * hh;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vp = &sm.vt[(32 * db + l32) * AttnSmem<D>::VP + kcol];
+          const uint16_t* vp = &b.vt[(32 * db + l32) * AttnSmem<D>::VP + kcol];
           const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
           const u32x4 a4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
@@ -270,18 +310,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
       }
     }
 
+    if (more) store_tile(sm[(t + 1) & 1]);
     __syncthreads();
-    if (more) {
-      store_tile();
-      __syncthreads();
-    }
   }
 
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  const bool empty = !(l_tot > 0.0f) || m_run == -INFINITY;  // no visible key
+  const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (q_ok) {
-    uint16_t* op = out + static_cast<int64_t>(my_q) * q_stride + static_cast<int64_t>(head) * D;
+    uint16_t* op = out + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
@@ -292,10 +330,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * j + 4 * hh) = w;
       }
     }
-    if (lse != nullptr && hh == 0) {
-      const float L = l_tot > 0.0f ? kLn2 * (cr * (m_run == -INFINITY ? 0.0f : m_run) + log2f(l_tot)) : -INFINITY;
-      lse[static_cast<int64_t>(head) * N + my_q] = L;
-    }
+    if (lse != nullptr && hh == 0)
+      lse[static_cast<int64_t>(head) * N + my_q] =
+          empty ? -INFINITY : kLn2 * (m_run + __builtin_log2f(l_tot));
   }
 }
 
@@ -409,6 +446,10 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
                 (long long)D);
   if (N * Hq > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: N * Hq must fit in int32");
+  if (dt == TG_DTYPE_BF16 && N * Hq * D * 2 > kMaxTokens)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_bias_attn_fwd: bf16 path addresses Q/K/V with 32-bit offsets "
+                "(N * Hq * D * 2 must be < 2^31)");
   if (N == 0) {
     clear_error();
     return TG_OK;
@@ -444,7 +485,7 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   const auto* kb = static_cast<const uint16_t*>(k);
   const auto* vb = static_cast<const uint16_t*>(v);
   auto* ob = static_cast<uint16_t*>(out);
-  const float sl2 = scale * kLog2e;
+  const float sl2 = scale;
   const bool cz = causal != 0, hb = key_score != nullptr, hs = q_scale != nullptr;
 #define TG_ATTN_DISPATCH(DD, HH) \
   launch_bf16_attn_c<DD, HH>(cz, hb, hs, n, hq, hkv, s, qb, kb, vb, key_score, gain, q_scale, sl2, ob, lse)

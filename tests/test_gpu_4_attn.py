@@ -107,6 +107,7 @@ def test_attn_zero_bias_equals_no_bias_bitwise():
 
 
 def test_attn_row0_is_v0_exactly():
+    """Row 0 sees only key 0, whose weight is exactly 1: O[0] = V[0] bitwise."""
     rng = np.random.default_rng(81)
     q, k, v, s, g, c = make(rng, 70, 8, 4, 128, "bf16")
     o, _ = gpu(q, k, v, s, g, c, "bf16")
