@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with the last-level cache flushed before each")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy, the reference kernel that "
+                         "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (the path runs on one "
@@ -207,6 +210,14 @@ def main():
         check(lib.tg_bias_attn_fwd(*att_args), "tg_bias_attn_fwd")
         if ev is not None:
             ev[4].record(stream)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()

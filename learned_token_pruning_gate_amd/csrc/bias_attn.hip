@@ -160,7 +160,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   // weight underflows to exactly 0, as deleting the key would give.
   const float masked_bias = -2097152.0f * inv_scale / kLog2e;
   u32x4 kreg[KI], vreg[4];
-  u32x2 breg = u32x2{0, 0};
+  float sreg = 0.0f;        // staged raw score (its bias is formed at store time)
+  const int bias_key = tid % kBK;
+  const float bias_gain = (HAS_BIAS && tid < HPW * kBK) ? gain[hg * HPW + tid / kBK] : 0.0f;
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(key_score), 0, HAS_BIAS ? N * 4 : 0, 0x00020000);
   auto load_tile = [&](int t) {
     const int k0 = t * kBK;
     const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
@@ -174,12 +178,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(
             v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
     }
-    if (HAS_BIAS && tid < HPW * kBK) {
-      const int key = k0 + (tid % kBK);
-      const float sc = key < N ? key_score[key] : 0.0f;
-      breg = split_bf16_triple(sc == -INFINITY ? masked_bias
-                                               : gain[hg * HPW + tid / kBK] * sc * inv_scale);
-    }
+    if (HAS_BIAS && tid < HPW * kBK)   // keys past N read 0
+      sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           s_rs, 4u * static_cast<uint32_t>(k0 + bias_key), 0, 0));
   };
   auto store_tile = [&](AttnSmem<D>& b) {
 #pragma unroll
@@ -198,7 +199,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + 4 * vkg]) = hi;
       }
     }
-    if (HAS_BIAS && tid < HPW * kBK) b.bias[tid / kBK][tid % kBK] = breg;
+    if (HAS_BIAS && tid < HPW * kBK)
+      b.bias[tid / kBK][bias_key] = split_bf16_triple(
+          sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale);
   };
 
   // ---- running state --------------------------------------------------------
@@ -218,6 +221,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     const int k0 = t * kBK;
     const bool more = t + 1 < n_tiles;
     if (more) load_tile(t + 1);
+    // keep the next tile's loads issued here, ahead of this tile's math
+    __builtin_amdgcn_sched_barrier(0);
 
     // S'^T = K' Q'^T = <q, k> + bias'
     f32x16 s[2];

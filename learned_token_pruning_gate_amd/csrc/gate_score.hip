@@ -14,9 +14,10 @@
 //     W1 (gamma * x / rms) = (W1 (gamma * x)) / rms, so the row's sum of
 //     squares is accumulated from the same registers that stage the tile;
 //   * a workgroup owns TM rows and all h outputs; the TM x 64 residual tile
-//     of each k-stage goes HBM -> registers -> padded LDS (double buffered,
-//     one barrier per stage) and is read by the four waves as MFMA A
-//     operands;
+//     of each k-stage goes HBM -> registers (two stages in flight, loaded
+//     non-temporally so the stream does not evict W1 from L2) -> padded LDS
+//     (double buffered, one barrier per stage) and is read by the four waves
+//     as MFMA A operands;
 //   * each wave owns h/4 output columns and streams its slice of W1 (which
 //     stays resident in each XCD's L2) straight into registers as MFMA B
 //     operands, one stage ahead;
@@ -31,6 +32,7 @@ namespace tg {
 namespace {
 
 constexpr int kKS = 64;                 // k elements per stage
+constexpr int kMaxGammaD = 8192;        // largest d with an RMSNorm weight (LDS-staged)
 constexpr int kPitch = kKS + 8;         // LDS row pitch in bf16 (144 bytes)
 
 template <int TM, int NT, bool HAS_GAMMA>
@@ -42,6 +44,7 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   constexpr int RPT = TM / 32;          // staged rows per thread
   constexpr int MT = TM / 16;           // 16-row MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kPitch];
+  __shared__ __attribute__((aligned(16))) float s_gamma[HAS_GAMMA ? kMaxGammaD : 1];
   __shared__ float s_rs[TM];
   __shared__ float s_part[4][TM];
   __shared__ int s_any;
@@ -51,17 +54,32 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   const int wave = tid >> 6;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * TM;
 
-  // staging role: row (tid/8) + 32 i, 16-byte chunk tid % 8 of the stage
+  // staging role: row (tid/8) + 32 i, 16-byte chunk tid % 8 of the stage.
+  // Loads go through buffer resources: an offset past the end reads zeros,
+  // so rows that are not prunable (or past T) and the k tail need no branch.
   const int chunk = tid & 7;
+  constexpr uint32_t kOff = 0x80000000u;   // beyond every resource below
   bool live[RPT];
-  const uint16_t* xrow[RPT];
+  uint32_t xoff[RPT];                      // byte offset of the row's chunk, or kOff
   int any = 0;
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
-    const int64_t r = row0 + (tid >> 3) + 32 * i;
-    live[i] = (r < T) && prunable[r] != 0;
+    const int r = (tid >> 3) + 32 * i;
+    live[i] = (row0 + r < T) && prunable[row0 + r] != 0;
     any |= live[i];
-    xrow[i] = resid + (live[i] ? r : 0) * ld_x + chunk * 8;
+    xoff[i] = live[i] ? static_cast<uint32_t>(r) * static_cast<uint32_t>(ld_x) * 2u + chunk * 16u
+                      : kOff;
+  }
+  const int64_t rows_here = T - row0 < TM ? T - row0 : TM;
+  const __amdgpu_buffer_rsrc_t x_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(resid + row0 * ld_x), 0,
+      static_cast<int>(static_cast<uint32_t>(((rows_here - 1) * ld_x + d) * 2)), 0x00020000);
+  const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w1), 0, static_cast<int>(static_cast<uint32_t>(NT * 64 * d * 2)),
+      0x00020000);
+  if (HAS_GAMMA) {   // RMSNorm weight staged once; read from LDS per stage
+    for (int i = tid; i < d; i += 256) s_gamma[i] = gamma[i];
+    __syncthreads();
   }
   if (tid == 0) s_any = 0;
   __syncthreads();
@@ -76,36 +94,40 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   const int hbase = wave * 16 * NT;
   const int lrow = lane & 15;            // A row / B column inside a 16x16 tile
   const int lk = (lane >> 4) * 8;        // k offset of this lane's 8 elements
-  const uint16_t* wrow[NT];
+  uint32_t woff[NT];                     // byte offset of this lane's W1 row at k = lk
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wrow[nt] = w1 + static_cast<int64_t>(hbase + nt * 16 + lrow) * d + lk;
+  for (int nt = 0; nt < NT; ++nt)
+    woff[nt] = (static_cast<uint32_t>(hbase + nt * 16 + lrow) * static_cast<uint32_t>(d) + lk) * 2u;
 
   const int nstages = (d + kKS - 1) / kKS;
   float ss[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) ss[i] = 0.0f;
 
-  u32x4 xr[RPT];
-  auto load_x = [&](int s) {
-    const int k = s * kKS + chunk * 8;
+  // two register sets: stage s+2 is in flight while stage s+1 is stored
+  u32x4 xr[2][RPT];
+  auto load_x = [&](int s, u32x4 (&dst)[RPT]) {
+    const bool kin = s * kKS + chunk * 8 < d;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      if (live[i] && k < d)
-        xr[i] = *reinterpret_cast<const u32x4*>(xrow[i] + s * kKS);
-      else
-        xr[i] = u32x4{0, 0, 0, 0};
-    }
+    for (int i = 0; i < RPT; ++i)   // streamed once (non-temporal)
+      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+          x_rs, kin ? xoff[i] + static_cast<uint32_t>(s) * kKS * 2u : kOff, 0, 2);
   };
-  auto store_x = [&](int s, int buf) {
-    const int k = s * kKS + chunk * 8;
+  auto store_x = [&](int s, int buf, const u32x4 (&src)[RPT]) {
     float g[8];
     if (HAS_GAMMA) {
+      const int k = s * kKS + chunk * 8;   // rows past d are zero, any gamma works
+      const f32x4 g0 = *reinterpret_cast<const f32x4*>(&s_gamma[k < d ? k : 0]);
+      const f32x4 g1 = *reinterpret_cast<const f32x4*>(&s_gamma[(k < d ? k : 0) + 4]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) g[e] = (k + e < d) ? gamma[k + e] : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        g[e] = g0[e];
+        g[4 + e] = g1[e];
+      }
     }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      u32x4 v = xr[i];
+      u32x4 v = src[i];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float lo = __uint_as_float(v[e] << 16);
@@ -124,18 +146,17 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
     }
   };
 
-  bf16x8 wc[NT][2], wn[NT][2];
-  auto load_w = [&](int s, bf16x8 (&w)[NT][2]) {
+  // W1 fragments stay integer vectors until they reach the MFMA (bf16 vector
+  // values would pick up extra register operations right after the load)
+  u32x4 wc[NT][2], wn[NT][2];
+  auto load_w = [&](int s, u32x4 (&w)[NT][2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int k = s * kKS + kk * 32 + lk;
+      const bool kin = s * kKS + kk * 32 + lk < d;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        if (k < d)
-          w[nt][kk] = *reinterpret_cast<const bf16x8*>(wrow[nt] + s * kKS + kk * 32);
-        else
-          w[nt][kk] = bf16x8{};
-      }
+      for (int nt = 0; nt < NT; ++nt)
+        w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+            w_rs, kin ? woff[nt] + static_cast<uint32_t>(s * kKS + kk * 32) * 2u : kOff, 0, 0);
     }
   };
 
@@ -145,38 +166,42 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_x(0);
+  load_x(0, xr[0]);
+  load_x(1, xr[1]);
   load_w(0, wc);
-  store_x(0, 0);
+  store_x(0, 0, xr[0]);
   __syncthreads();
 
-  for (int s = 0; s < nstages; ++s) {
+  // One stage: prefetch x(s+2) and W1(s+1), multiply stage s out of LDS
+  // buffer s&1 with W1(s), then stage x(s+1) into the other buffer.  Every
+  // stage runs unconditionally: loads past d read zeros, which leave the
+  // accumulators and sums of squares unchanged, and straight-line loads let
+  // the compiler wait for exactly the data each step needs.
+  auto stage = [&](int s, const u32x4 (&wcur)[NT][2], u32x4 (&wnext)[NT][2]) {
     const int buf = s & 1;
-    const bool more = s + 1 < nstages;
-    if (more) {
-      load_x(s + 1);
-      load_w(s + 1, wn);
-    }
+    load_x(s + 2, xr[buf]);
+    load_w(s + 1, wnext);
+    // keep the prefetches issued here: the scheduler would otherwise sink them
+    // next to their uses and serialise the pipeline
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8*>(&xs[buf][(mt * 16 + lrow) * kPitch + kk * 32 + lk]);
+        const bf16x8 a = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(&xs[buf][(mt * 16 + lrow) * kPitch + kk * 32 + lk]));
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, wc[nt][kk], acc[mt][nt], 0, 0, 0);
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              a, __builtin_bit_cast(bf16x8, wcur[nt][kk]), acc[mt][nt], 0, 0, 0);
       }
     }
-    if (more) store_x(s + 1, buf ^ 1);
+    store_x(s + 1, buf ^ 1, xr[buf ^ 1]);
     __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        wc[nt][0] = wn[nt][0];
-        wc[nt][1] = wn[nt][1];
-      }
-    }
+  };
+  for (int s = 0; s < nstages; s += 2) {   // an odd count runs one all-zero stage
+    stage(s, wc, wn);
+    stage(s + 1, wn, wc);
   }
 
   // per-row 1/rms: reduce the sum of squares over the 8 lanes of a row
@@ -326,6 +351,12 @@ extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_gate_score: bf16 path needs h in {64, 128, 192, 256} (h=%lld)",
                 (long long)h);
+  if (rms_weight != nullptr && d > kMaxGammaD)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gate_score: bf16 path with an RMSNorm weight needs d <= %d",
+                kMaxGammaD);
+  if (static_cast<int64_t>(64) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_gate_score: bf16 path addresses a 64-row tile and W1 with 31-bit offsets");
   if (!aligned(resid, 16) || !aligned(w1, 16) || (resid_row_stride % 8) != 0)
     return fail(TG_ERR_INVALID_ARGUMENT,
                 "tg_gate_score: bf16 resid/w1 must be 16-byte aligned, row stride %% 8 == 0");
