@@ -123,6 +123,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with the last-level cache flushed before each")
+    ap.add_argument("--rms-weight", action="store_true",
+                    help="pass the workload's RMSNorm weight explicitly; by default it is "
+                         "NULL, which the ABI defines as all ones (the workload's weight)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel that "
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -179,7 +182,8 @@ def main():
     dtc = tg.TG_DTYPE_BF16 if dt == "bf16" else tg.TG_DTYPE_F32
     key_ptr = P(drawn) if drawn is not None else P(score_kept)
     F = ctypes.c_float
-    gate_args = (dtc, w.T, w.d, w.h, P(resid), resid.stride(0), P(prunable), P(gamma),
+    gate_args = (dtc, w.T, w.d, w.h, P(resid), resid.stride(0), P(prunable),
+                 P(gamma) if args.rms_weight else None,
                  F(g.eps), P(w1), P(b1), P(w2), F(g.b2), P(scores), sp)
     sel_args = (w.T, P(scores), P(prunable), w.K, P(kept), kept.numel(), P(n_kept), P(ws),
                 ws.numel(), sp)

@@ -32,11 +32,19 @@ namespace tg {
 namespace {
 
 constexpr int kKS = 64;                 // k elements per stage
-constexpr int kMaxGammaD = 8192;        // largest d with an RMSNorm weight (LDS-staged)
+#ifndef TG_GATE_TM
+#define TG_GATE_TM 64                   // residual rows per workgroup
+#endif
 constexpr int kPitch = kKS + 8;         // LDS row pitch in bf16 (144 bytes)
 
-template <int TM, int NT, bool HAS_GAMMA>
-__global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
+#ifndef TG_GATE_MINWG
+#define TG_GATE_MINWG 2                 // workgroups per CU the registers are sized for
+#endif
+
+// FAST: d is a multiple of 2 * kKS, so every stage is full; per-lane load
+// offsets are fixed and the stage advance is the instruction's scalar offset.
+template <int TM, int NT, bool HAS_GAMMA, bool FAST>
+__global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     const float* __restrict__ gamma, float eps, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2,
@@ -44,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   constexpr int RPT = TM / 32;          // staged rows per thread
   constexpr int MT = TM / 16;           // 16-row MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kPitch];
-  __shared__ __attribute__((aligned(16))) float s_gamma[HAS_GAMMA ? kMaxGammaD : 1];
+  extern __shared__ __attribute__((aligned(16))) float s_gamma[];   // [d] when HAS_GAMMA
   __shared__ float s_rs[TM];
   __shared__ float s_part[4][TM];
   __shared__ int s_any;
@@ -107,11 +115,17 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   // two register sets: stage s+2 is in flight while stage s+1 is stored
   u32x4 xr[2][RPT];
   auto load_x = [&](int s, u32x4 (&dst)[RPT]) {
-    const bool kin = s * kKS + chunk * 8 < d;
+    if (FAST) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)   // streamed once (non-temporal)
-      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          x_rs, kin ? xoff[i] + static_cast<uint32_t>(s) * kKS * 2u : kOff, 0, 2);
+      for (int i = 0; i < RPT; ++i)   // streamed once (non-temporal)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xoff[i], s * kKS * 2, 2);
+    } else {
+      const bool kin = s * kKS + chunk * 8 < d;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            x_rs, kin ? xoff[i] + static_cast<uint32_t>(s) * kKS * 2u : kOff, 0, 2);
+    }
   };
   auto store_x = [&](int s, int buf, const u32x4 (&src)[RPT]) {
     float g[8];
@@ -152,11 +166,19 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   auto load_w = [&](int s, u32x4 (&w)[NT][2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const bool kin = s * kKS + kk * 32 + lk < d;
+      if (FAST) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(
-            w_rs, kin ? woff[nt] + static_cast<uint32_t>(s * kKS + kk * 32) * 2u : kOff, 0, 0);
+        for (int nt = 0; nt < NT; ++nt)
+          w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, woff[nt] + kk * 64,
+                                                            s * kKS * 2, 0);
+      } else {
+        const bool kin = s * kKS + kk * 32 + lk < d;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(
+              w_rs, kin ? woff[nt] + static_cast<uint32_t>(s * kKS + kk * 32) * 2u : kOff, 0,
+              0);
+      }
     }
   };
 
@@ -167,7 +189,7 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   load_x(0, xr[0]);
-  load_x(1, xr[1]);
+  if (!FAST || nstages > 1) load_x(1, xr[1]);
   load_w(0, wc);
   store_x(0, 0, xr[0]);
   __syncthreads();
@@ -177,10 +199,12 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
   // stage runs unconditionally: loads past d read zeros, which leave the
   // accumulators and sums of squares unchanged, and straight-line loads let
   // the compiler wait for exactly the data each step needs.
-  auto stage = [&](int s, const u32x4 (&wcur)[NT][2], u32x4 (&wnext)[NT][2]) {
+  // PREF: issue this stage's prefetches (the FAST epilogue stages do not).
+  auto stage = [&](int s, const u32x4 (&wcur)[NT][2], u32x4 (&wnext)[NT][2], bool pref_x,
+                   bool pref_w, bool stage_next) {
     const int buf = s & 1;
-    load_x(s + 2, xr[buf]);
-    load_w(s + 1, wnext);
+    if (pref_x) load_x(s + 2, xr[buf]);
+    if (pref_w) load_w(s + 1, wnext);
     // keep the prefetches issued here: the scheduler would otherwise sink them
     // next to their uses and serialise the pipeline
     __builtin_amdgcn_sched_barrier(0);
@@ -196,12 +220,23 @@ __global__ __launch_bounds__(256, 2) void gate_bf16_kernel(
               a, __builtin_bit_cast(bf16x8, wcur[nt][kk]), acc[mt][nt], 0, 0, 0);
       }
     }
-    store_x(s + 1, buf ^ 1, xr[buf ^ 1]);
+    if (stage_next) store_x(s + 1, buf ^ 1, xr[buf ^ 1]);
     __syncthreads();
   };
-  for (int s = 0; s < nstages; s += 2) {   // an odd count runs one all-zero stage
-    stage(s, wc, wn);
-    stage(s + 1, wn, wc);
+  if (FAST) {
+    // steady state: stages 0 .. nstages-3 with every prefetch in range, then
+    // two epilogue stages without prefetch (nstages is even and >= 2)
+    for (int s = 0; s + 2 < nstages; s += 2) {
+      stage(s, wc, wn, true, true, true);
+      stage(s + 1, wn, wc, s + 3 < nstages, true, true);
+    }
+    stage(nstages - 2, wc, wn, false, true, true);
+    stage(nstages - 1, wn, wc, false, false, false);
+  } else {
+    for (int s = 0; s < nstages; s += 2) {   // an odd count runs one all-zero stage
+      stage(s, wc, wn, true, true, true);
+      stage(s + 1, wn, wc, true, true, true);
+    }
   }
 
   // per-row 1/rms: reduce the sum of squares over the 8 lanes of a row
@@ -295,16 +330,26 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(
   if (lane == 0) scores[t] = b2 + part;
 }
 
+template <int TM, int NT, bool FAST>
+void launch_bf16_f(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint16_t* x,
+                   int64_t ld, const uint8_t* p, const float* g, float eps, const uint16_t* w1,
+                   const float* b1, const float* w2, float b2, float* out, int32_t d) {
+  if (has_gamma)
+    gate_bf16_kernel<TM, NT, true, FAST><<<grid, dim3(256), static_cast<size_t>(d) * 4, s>>>(
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+  else
+    gate_bf16_kernel<TM, NT, false, FAST><<<grid, dim3(256), 0, s>>>(
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+}
+
 template <int TM, int NT>
 void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint16_t* x,
                  int64_t ld, const uint8_t* p, const float* g, float eps, const uint16_t* w1,
                  const float* b1, const float* w2, float b2, float* out, int32_t d) {
-  if (has_gamma)
-    gate_bf16_kernel<TM, NT, true><<<grid, dim3(256), 0, s>>>(
-        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+  if (d % (2 * kKS) == 0)
+    launch_bf16_f<TM, NT, true>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d);
   else
-    gate_bf16_kernel<TM, NT, false><<<grid, dim3(256), 0, s>>>(
-        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+    launch_bf16_f<TM, NT, false>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d);
 }
 
 }  // namespace
@@ -351,10 +396,10 @@ extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_gate_score: bf16 path needs h in {64, 128, 192, 256} (h=%lld)",
                 (long long)h);
-  if (rms_weight != nullptr && d > kMaxGammaD)
-    return fail(TG_ERR_UNSUPPORTED, "tg_gate_score: bf16 path with an RMSNorm weight needs d <= %d",
-                kMaxGammaD);
-  if (static_cast<int64_t>(64) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
+  if (rms_weight != nullptr && d > 16384)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_gate_score: bf16 path with an RMSNorm weight needs d <= 16384 (LDS-staged)");
+  if (static_cast<int64_t>(TG_GATE_TM) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_gate_score: bf16 path addresses a 64-row tile and W1 with 31-bit offsets");
   if (!aligned(resid, 16) || !aligned(w1, 16) || (resid_row_stride % 8) != 0)
@@ -364,7 +409,7 @@ extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
   const auto* w = static_cast<const uint16_t*>(w1);
   const int32_t d32 = static_cast<int32_t>(d);
   const bool g = rms_weight != nullptr;
-  constexpr int TM = 64;
+  constexpr int TM = TG_GATE_TM;
   const dim3 grid(static_cast<uint32_t>((T + TM - 1) / TM));
   switch (h / 64) {
     case 1: launch_bf16<TM, 1>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
