@@ -13,6 +13,8 @@
  * their attention logits.  This library is that path's hot core:
  *
  *   tg_gate_score      RMSNorm + MLP scorer over the residual rows   [a1]
+ *   tg_gate_pack_w1 / tg_gate_score_packed
+ *                      the same scorer with W1 packed once at load   [a1]
  *   tg_topk_select     top-K selection and ordered compaction        [a2,a3]
  *   tg_compact_gather  gather of residual rows/positions/scores      [a4]
  *   tg_bias_attn_fwd   causal GQA attention with the gate bias       [a5]
@@ -93,6 +95,39 @@ tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
                         float eps, const void* w1, const float* b1,
                         const float* w2, float b2, float* scores,
                         void* stream);
+
+/* --------------------------------------------------------------------------
+ * [a1] Gate scorer with a packed W1.  The same operation as tg_gate_score
+ * (same pages, same formula) for the bf16 path with a unit RMSNorm weight.
+ * W1 is a constant of the trained gate, so it can be rearranged once, when
+ * the weights are loaded, into the order in which the scorer's matrix-core
+ * instructions consume it: then each 64-wide slice of the hidden dimension
+ * is one contiguous block instead of h rows d*2 bytes apart.  The packed
+ * bytes are an opaque layout (a permutation of W1's elements, no rounding);
+ * only tg_gate_score_packed reads them.  Results equal tg_gate_score's for
+ * the same W1, up to fp32 summation order.
+ *
+ * tg_gate_w1_packed_bytes  bytes of the packed W1 for (dt, h, d), or 0 when
+ *             the layout does not cover them (it needs dt == TG_DTYPE_BF16,
+ *             d % 64 == 0, d >= 128, h in {64, 128, 192, 256}).
+ * tg_gate_pack_w1  reads w1 [h][d] bf16 (row-major, 16-byte aligned) and
+ *             writes w1_packed (tg_gate_w1_packed_bytes bytes, 16-byte
+ *             aligned, not overlapping w1).  Enqueued on `stream`.
+ * tg_gate_score_packed  arguments as tg_gate_score, with w1_packed in place
+ *             of w1; dt must be TG_DTYPE_BF16 and rms_weight NULL
+ *             (TG_ERR_UNSUPPORTED otherwise).
+ * ------------------------------------------------------------------------ */
+size_t tg_gate_w1_packed_bytes(tg_dtype dt, int64_t h, int64_t d);
+
+tg_status tg_gate_pack_w1(tg_dtype dt, int64_t h, int64_t d, const void* w1,
+                          void* w1_packed, void* stream);
+
+tg_status tg_gate_score_packed(tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                               const void* resid, int64_t resid_row_stride,
+                               const uint8_t* prunable, const float* rms_weight,
+                               float eps, const void* w1_packed, const float* b1,
+                               const float* w2, float b2, float* scores,
+                               void* stream);
 
 /* --------------------------------------------------------------------------
  * [a2, a3] Top-K selection and order-preserving compaction.  Pages: ai.info

@@ -9,6 +9,9 @@ GPU, the call raises.
 Entry points (same names as the C ABI):
 
 * ``tg_gate_score``       -- RMSNorm + MLP scorer over the residual rows
+* ``tg_gate_w1_packed_bytes`` / ``tg_gate_pack_w1`` / ``tg_gate_score_packed``
+                          -- the same scorer with W1 packed once, at weight
+                             load, into the MFMA fragment order
 * ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
 * ``tg_compact_gather``   -- gather of rows, positions and scores
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
@@ -22,7 +25,8 @@ import torch
 
 __all__ = [
     "TokenGateError", "lib_path", "load", "kept_count",
-    "tg_status_str", "tg_last_error", "tg_gate_score", "tg_topk_workspace_size",
+    "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
+    "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
     "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
     "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
@@ -34,7 +38,8 @@ lib_path = os.path.join(_HERE, "libtokengate.so")
 TG_OK, TG_ERR_INVALID_ARGUMENT, TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, TG_ERR_LAUNCH = range(5)
 TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 
-EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_topk_workspace_size",
+EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
+            "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
             "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd")
 
 
@@ -64,6 +69,12 @@ def load():
     lib.tg_last_error.restype = ctypes.c_char_p
     lib.tg_gate_score.argtypes = [I, I64, I64, I64, P, I64, P, P, F, P, P, P, F, P, P]
     lib.tg_gate_score.restype = I
+    lib.tg_gate_score_packed.argtypes = [I, I64, I64, I64, P, I64, P, P, F, P, P, P, F, P, P]
+    lib.tg_gate_score_packed.restype = I
+    lib.tg_gate_w1_packed_bytes.argtypes = [I, I64, I64]
+    lib.tg_gate_w1_packed_bytes.restype = ctypes.c_size_t
+    lib.tg_gate_pack_w1.argtypes = [I, I64, I64, P, P, P]
+    lib.tg_gate_pack_w1.restype = I
     lib.tg_topk_workspace_size.argtypes = [I64]
     lib.tg_topk_workspace_size.restype = ctypes.c_size_t
     lib.tg_topk_select.argtypes = [I64, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]
@@ -154,6 +165,54 @@ def tg_gate_score(resid, prunable, w1, w2, b2=0.0, rms_weight=None, b1=None, eps
                            _ptr(rms_weight), float(eps), _ptr(w1), _ptr(b1), _ptr(w2),
                            float(b2), _ptr(scores), _stream(stream))
     _check(st, "tg_gate_score")
+    return scores
+
+
+def tg_gate_w1_packed_bytes(dtype, h: int, d: int) -> int:
+    """Bytes of the packed W1 layout (0 if that layout does not cover h, d)."""
+    dt = TG_DTYPE_BF16 if dtype == torch.bfloat16 else TG_DTYPE_F32
+    return int(load().tg_gate_w1_packed_bytes(dt, int(h), int(d)))
+
+
+def tg_gate_pack_w1(w1, out=None, stream=None):
+    """Packed copy of a contiguous bf16 W1 [h, d] (a flat bf16 tensor)."""
+    lib = load()
+    _dev(w1, "w1", torch.bfloat16)
+    if w1.dim() != 2 or not w1.is_contiguous():
+        raise ValueError("w1 must be a contiguous [h, d] tensor")
+    h, d = w1.shape
+    if out is None:
+        out = torch.empty(h * d, dtype=torch.bfloat16, device=w1.device)
+    _dev(out, "out", torch.bfloat16)
+    if out.numel() * 2 < tg_gate_w1_packed_bytes(torch.bfloat16, h, d):
+        raise ValueError("out holds fewer bytes than the packed layout")
+    _check(lib.tg_gate_pack_w1(TG_DTYPE_BF16, h, d, _ptr(w1), _ptr(out), _stream(stream)),
+           "tg_gate_pack_w1")
+    return out
+
+
+def tg_gate_score_packed(resid, prunable, w1_packed, w2, b2=0.0, b1=None, eps=1e-6,
+                         scores=None, stream=None):
+    """tg_gate_score with W1 from tg_gate_pack_w1; h is w2's length."""
+    lib = load()
+    _dev(resid, "resid", torch.bfloat16)
+    T, d = resid.shape
+    if resid.stride(1) != 1:
+        raise ValueError("resid rows must be contiguous")
+    _dev(prunable, "prunable", torch.uint8)
+    _dev(w2, "w2", torch.float32)
+    h = w2.shape[0]
+    _dev(w1_packed, "w1_packed", torch.bfloat16)
+    if w1_packed.numel() != h * d or not w1_packed.is_contiguous():
+        raise ValueError("w1_packed must be the contiguous output of tg_gate_pack_w1")
+    _dev(b1, "b1", torch.float32, allow_none=True)
+    if scores is None:
+        scores = torch.empty(T, dtype=torch.float32, device=resid.device)
+    _dev(scores, "scores", torch.float32)
+    st = lib.tg_gate_score_packed(TG_DTYPE_BF16, T, d, h, _ptr(resid), resid.stride(0),
+                                  _ptr(prunable), None, float(eps), _ptr(w1_packed), _ptr(b1),
+                                  _ptr(w2), float(b2), _ptr(scores), _stream(stream))
+    _check(st, "tg_gate_score_packed")
     return scores
 
 

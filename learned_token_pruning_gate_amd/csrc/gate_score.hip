@@ -114,11 +114,16 @@ __global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
 
   // two register sets: stage s+2 is in flight while stage s+1 is stored
   u32x4 xr[2][RPT];
+  // FAST: stages are walked in a rotated order per workgroup (see the DMA
+  // kernel: power-of-two row strides put one k slice in few L2 channels).
+  const int rot = FAST ? static_cast<int>((blockIdx.x >> 3) % static_cast<uint32_t>(nstages)) : 0;
+  auto phys = [&](int s) { const int k = s + rot; return k >= nstages ? k - nstages : k; };
   auto load_x = [&](int s, u32x4 (&dst)[RPT]) {
     if (FAST) {
+      const int ps = phys(s);
 #pragma unroll
       for (int i = 0; i < RPT; ++i)   // streamed once (non-temporal)
-        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xoff[i], s * kKS * 2, 2);
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(x_rs, xoff[i], ps * kKS * 2, 2);
     } else {
       const bool kin = s * kKS + chunk * 8 < d;
 #pragma unroll
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
   auto store_x = [&](int s, int buf, const u32x4 (&src)[RPT]) {
     float g[8];
     if (HAS_GAMMA) {
-      const int k = s * kKS + chunk * 8;   // rows past d are zero, any gamma works
+      const int k = (FAST ? phys(s) : s) * kKS + chunk * 8;   // past d: x is zero
       const f32x4 g0 = *reinterpret_cast<const f32x4*>(&s_gamma[k < d ? k : 0]);
       const f32x4 g1 = *reinterpret_cast<const f32x4*>(&s_gamma[(k < d ? k : 0) + 4]);
 #pragma unroll
@@ -167,10 +172,11 @@ __global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       if (FAST) {
+        const int ps = phys(s);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, woff[nt] + kk * 64,
-                                                            s * kKS * 2, 0);
+                                                            ps * kKS * 2, 0);
       } else {
         const bool kin = s * kKS + kk * 32 + lk < d;
 #pragma unroll
@@ -293,6 +299,309 @@ __global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streaming pipeline (no RMSNorm weight, d % 64 == 0, d >= 128).  Measured on
+// gfx950, the register/LDS kernel above is bound by on-chip traffic rather
+// than by HBM: every workgroup re-reads all of W1 from L2, and routing both
+// operands through LDS puts more bytes through the LDS port than the MFMA
+// pipes can use.  This kernel gives each operand the path that moves it once:
+//   * the residual tile (64 rows, shared by every wave) goes HBM -> LDS with
+//     gfx950's direct-to-LDS loads, 1 KiB MFMA A fragments in lane order,
+//     into a ring of DEPTH+1 64-k stages, DEPTH of them in flight;
+//   * each wave owns NTW 16-column tiles of h and streams only its own W1
+//     B fragments straight into registers, DEPTH stages ahead, never through
+//     LDS.  W1 is read either row-major ([h, d]) or in the packed layout that
+//     tg_gate_pack_w1 writes, where one stage's fragments are one contiguous
+//     block (row-major fragments gather 16 rows 4 KiB apart);
+//   * LDS traffic per stage is the tile written once and read by each wave:
+//     (1 + NW) * 8 KiB, against 16 MFMAs per wave.
+// The compiler does not track the direct loads, so waits are explicit: a wave
+// waits for its own loads of stage s (s_waitcnt vmcnt), then one barrier per
+// stage makes every wave's stage visible and frees the slot of stage s-1.
+// The row's sum of squares comes from the A fragments read back.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) {
+  return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);   // lgkmcnt/expcnt: no wait
+}
+constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);    // lgkmcnt(0) only
+
+#ifndef TG_GATE_DEPTH
+#define TG_GATE_DEPTH 4                 // k-stages in flight in the streaming kernel
+#endif
+
+struct XSlot {
+  u32x4 b[8][64];   // (row tile mt, k half kk) -> block mt*2+kk, lane order
+};
+
+// Packed W1 (tg_gate_pack_w1): for stage ks = k / 64, column tile ht = n / 16
+// and k half kk, a 1 KiB block whose lane l holds W1[16 ht + l % 16]
+// [64 ks + 32 kk + 8 (l / 16) + e], e = 0..7.  Block (ks, ht, kk) starts at
+// element ((ks * (h / 16) + ht) * 2 + kk) * 512.
+__host__ __device__ constexpr int64_t packed_block(int64_t ks, int64_t ht, int64_t kk, int64_t h) {
+  return ((ks * (h / 16) + ht) * 2 + kk) * 512;
+}
+
+// SiLU(z) = z / (1 + e^-z) from the hardware base-2 exponential and
+// reciprocal (each within a few ulp): e^-z = 2^(-z log2 e).  Large |z| stays
+// finite: 2^+big = inf gives z * 0 = -0, 2^-big = 0 gives z.
+__device__ __forceinline__ float silu_fast(float z) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * kLog2e));
+}
+
+// NST > 0 fixes the number of 64-k stages (d = 64 * NST) at compile time; the
+// stages are then fully unrolled.  Either way every ring index is a
+// compile-time constant, so the slots are distinct LDS objects and the W1
+// register sets distinct registers: the compiler never merges their waits.
+template <int NTW, int NW, int NST, bool PACKED>
+__global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
+    const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
+    float eps, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
+    const float* __restrict__ w2, float b2, float* __restrict__ scores, int32_t T, int32_t d,
+    int32_t h) {
+  constexpr int TM = 64;
+  constexpr int DEPTH = TG_GATE_DEPTH;
+  constexpr int R = DEPTH + 1;                 // ring length
+  constexpr int XPW = 8 / NW;                  // residual blocks each wave loads per stage
+  constexpr int PER_STAGE = XPW + 2 * NTW;     // vector-memory instructions per wave per stage
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(DEPTH >= 2 && R <= 8 && PER_STAGE * (DEPTH - 1) <= 63, "ring shape");
+  __shared__ __attribute__((aligned(16))) XSlot xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7;
+  __shared__ float s_ss[2][TM];
+  __shared__ float s_rs[TM];
+  __shared__ float s_part[NW][TM];
+  __shared__ int s_any;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+  const int lrow = lane & 15;
+  const int lgrp = lane >> 4;
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * TM;
+
+  if (tid == 0) s_any = 0;
+  __syncthreads();
+  if (tid < TM && row0 + tid < T && prunable[row0 + tid]) s_any = 1;
+  __syncthreads();
+  if (!s_any) {
+    if (tid < TM && row0 + tid < T) scores[row0 + tid] = 0.0f;
+    return;
+  }
+
+  // residual blocks wave*XPW + i: row tile (block >> 1), k half (block & 1).
+  // Rows past T re-read row T-1 (valid memory); their scores are never stored.
+  const uint16_t* xsrc[2];   // XPW <= 2 (a fixed size: the direct-load builtin rejects a dependent type)
+#pragma unroll
+  for (int i = 0; i < XPW; ++i) {
+    const int blk = wave * XPW + i;
+    const int64_t r = row0 + 16 * (blk >> 1) + lrow;
+    xsrc[i] = resid + (r < T ? r : T - 1) * ld_x + 32 * (blk & 1) + 8 * lgrp;
+  }
+  // W1 through a buffer resource (offsets are 32-bit; the host checks h*d*2)
+  const __amdgpu_buffer_rsrc_t w_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(w1), 0, static_cast<int>(static_cast<uint32_t>(h) * d * 2u),
+      0x00020000);
+  const int ht0 = wave * NTW;   // this wave's first 16-column tile
+  uint32_t woff;                // byte offset of this lane's fragment of (stage 0, ht0, kk 0)
+  if (PACKED)
+    woff = static_cast<uint32_t>(packed_block(0, ht0, 0, h)) * 2u + lane * 16u;
+  else
+    woff = (static_cast<uint32_t>(16 * ht0 + lrow) * static_cast<uint32_t>(d) + 8 * lgrp) * 2u;
+  // byte step between the wave's fragments (nt, kk) and between stages
+  const uint32_t w_nt = PACKED ? 2048u : 32u * static_cast<uint32_t>(d);
+  const uint32_t w_kk = PACKED ? 1024u : 64u;
+  const uint32_t w_ks = PACKED ? static_cast<uint32_t>(h) * 128u : 128u;
+
+  const int nstages = NST > 0 ? NST : d / kKS;
+  // Each workgroup walks the k stages in a rotated order, so the workgroups
+  // of an XCD (block ids 8 apart) read different parts of W1 at a time.
+  const int rot = static_cast<int>((blockIdx.x >> 3) % static_cast<uint32_t>(nstages));
+
+  u32x4 wr[R][NTW][2];   // W1 fragments, one set per ring slot
+  auto issue = [&](int st, XSlot& sl, u32x4 (&w)[NTW][2]) {
+    int ks = st + rot;
+    ks = ks >= nstages ? ks - nstages : ks;
+#pragma unroll
+    for (int i = 0; i < XPW; ++i)
+      __builtin_amdgcn_global_load_lds(xsrc[i] + ks * kKS,
+                                       (__attribute__((address_space(3))) void*)&sl.b[wave * XPW + i][0],
+                                       16, 0, 0);
+    const uint32_t so = static_cast<uint32_t>(ks) * w_ks;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        w[nt][kk] = __builtin_amdgcn_raw_buffer_load_b128(w_rs, woff + nt * w_nt + kk * w_kk, so, 0);
+  };
+  auto wait_own = [&](int ahead) {   // own loads of a stage done; `ahead` later stages may be in flight
+    switch (ahead) {
+      case 0: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;
+      case 1: __builtin_amdgcn_s_waitcnt(vmcnt_imm(PER_STAGE)); break;
+      case 2: __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PER_STAGE)); break;
+      case 3: __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * PER_STAGE)); break;
+      case 4: __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PER_STAGE)); break;
+      case 5: __builtin_amdgcn_s_waitcnt(vmcnt_imm(5 * PER_STAGE)); break;
+      default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(6 * PER_STAGE)); break;
+    }
+  };
+
+  f32x4 acc[4][NTW];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Row sums of squares on the matrix cores: an A fragment times itself
+  // (as B) puts sum_k x_r,k^2 on the diagonal of the 16x16 product.  The
+  // products of bf16 values are exact in fp32, as on the vector ALUs.  With 8
+  // waves, wave w takes row tile w & 3 and k half w >> 2 of every stage; with
+  // 4 waves, wave w takes row tile w and both k halves.
+  f32x4 acc_ss = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int ss_tile = NW == 8 ? (wave & 3) : wave;
+  const int ss_half = NW == 8 ? (wave >> 2) : 0;
+
+  auto stage = [&](int s, const XSlot& sl, const u32x4 (&wc)[NTW][2], XSlot& nsl,
+                   u32x4 (&wn)[NTW][2]) {
+    const int last = nstages - 1;
+    wait_own(s + DEPTH - 1 <= last ? DEPTH - 1 : last - s);
+    // every wave's stage s has landed; every wave is done reading stage s-1
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
+    __builtin_amdgcn_s_barrier();
+    u32x4 av[2][4];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) av[kk][m] = sl.b[m * 2 + kk][lane];
+    u32x4 mine[2];   // this wave's sum-of-squares fragments (XPW of them)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < XPW) mine[i] = sl.b[ss_tile * 2 + (NW == 8 ? ss_half : i)][lane];
+    if (s + DEPTH <= last) issue(s + DEPTH, nsl, wn);
+    // keep the prefetch issued here, ahead of this stage's MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < XPW)
+        acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mine[i]),
+                                                         __builtin_bit_cast(bf16x8, mine[i]),
+                                                         acc_ss, 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, av[kk][m]), __builtin_bit_cast(bf16x8, wc[nt][kk]),
+              acc[m][nt], 0, 0, 0);
+    }
+  };
+  // slot j of the ring: LDS object xs<j>, register set wr[j]
+#define TG_STAGE_SLOT(S, J)                                                        \
+  stage((S), xs##J, wr[J], (J + DEPTH) % R == 0 ? xs0 : (J + DEPTH) % R == 1 ? xs1 \
+        : (J + DEPTH) % R == 2 ? xs2 : (J + DEPTH) % R == 3 ? xs3 : (J + DEPTH) % R == 4 ? xs4 \
+        : (J + DEPTH) % R == 5 ? xs5 : (J + DEPTH) % R == 6 ? xs6 : xs7, wr[(J + DEPTH) % R])
+  auto run = [&](int s, int j) {   // j == s % R, a constant after unrolling
+    switch (j) {
+      case 0: TG_STAGE_SLOT(s, 0); break;
+      case 1: TG_STAGE_SLOT(s, 1); break;
+      case 2: TG_STAGE_SLOT(s, 2); break;
+      case 3: if constexpr (R > 3) TG_STAGE_SLOT(s, 3); break;
+      case 4: if constexpr (R > 4) TG_STAGE_SLOT(s, 4); break;
+      case 5: if constexpr (R > 5) TG_STAGE_SLOT(s, 5); break;
+      case 6: if constexpr (R > 6) TG_STAGE_SLOT(s, 6); break;
+      default: if constexpr (R > 7) TG_STAGE_SLOT(s, 7); break;
+    }
+  };
+#undef TG_STAGE_SLOT
+  // prologue: stages 0 .. DEPTH-1 in flight (nstages >= 2; later ones guarded)
+  issue(0, xs0, wr[0]);
+  issue(1, xs1, wr[1]);
+  if constexpr (DEPTH > 2) if (2 < nstages) issue(2, xs2, wr[2 % R]);
+  if constexpr (DEPTH > 3) if (3 < nstages) issue(3, xs3, wr[3 % R]);
+  if constexpr (DEPTH > 4) if (4 < nstages) issue(4, xs4, wr[4 % R]);
+  if constexpr (DEPTH > 5) if (5 < nstages) issue(5, xs5, wr[5 % R]);
+  if constexpr (DEPTH > 6) if (6 < nstages) issue(6, xs6, wr[6 % R]);
+  if constexpr (NST > 0) {
+#pragma unroll
+    for (int s = 0; s < NST; ++s) run(s, s % R);
+  } else {
+    for (int s0 = 0; s0 < nstages; s0 += R) {
+#pragma unroll
+      for (int j = 0; j < R; ++j)
+        if (s0 + j < nstages) run(s0 + j, j);
+    }
+  }
+
+  // lane l holds rows 4 (l >> 4) + r, column l & 15 of the product: the
+  // diagonal entry of row i is lane 16 (i >> 2) + i, register i & 3
+  if (((lane & 15) >> 2) == lgrp) {
+    const int r = lane & 3;
+    const float v = r == 0 ? acc_ss[0] : r == 1 ? acc_ss[1] : r == 2 ? acc_ss[2] : acc_ss[3];
+    s_ss[ss_half][ss_tile * 16 + (lane & 15)] = v;
+  }
+  if (NW == 4 && tid < TM) s_ss[1][tid] = 0.0f;
+  __syncthreads();
+  if (tid < TM) s_rs[tid] = 1.0f / sqrtf((s_ss[0][tid] + s_ss[1][tid]) / static_cast<float>(d) + eps);
+  __syncthreads();
+
+  float part[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[m][r] = 0.0f;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    const int n = (ht0 + nt) * 16 + lrow;
+    const float bb = b1 ? b1[n] : 0.0f;
+    const float ww = w2[n];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float z = fmaf(acc[m][nt][r], s_rs[m * 16 + lgrp * 4 + r], bb);
+        part[m][r] = fmaf(ww, silu_fast(z), part[m][r]);
+      }
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = part[m][r];
+      v += __shfl_xor(v, 1, 64);
+      v += __shfl_xor(v, 2, 64);
+      v += __shfl_xor(v, 4, 64);
+      v += __shfl_xor(v, 8, 64);
+      if (lrow == 0) s_part[wave][m * 16 + lgrp * 4 + r] = v;
+    }
+  __syncthreads();
+  if (tid < TM) {
+    const int64_t t = row0 + tid;
+    if (t < T) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; w += 2) sc += s_part[w][tid] + s_part[w + 1][tid];
+      scores[t] = prunable[t] ? b2 + sc : 0.0f;
+    }
+  }
+}
+
+// tg_gate_pack_w1: one thread per 16-byte fragment of the packed layout.
+__global__ void gate_pack_w1_kernel(const uint16_t* __restrict__ w1, uint16_t* __restrict__ out,
+                                    int32_t h, int32_t d) {
+  const int64_t f = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;   // fragment
+  const int64_t nfrag = static_cast<int64_t>(h) * d / 8;
+  if (f >= nfrag) return;
+  const int l = static_cast<int>(f & 63);
+  const int64_t blk = f >> 6;                 // ((ks * (h/16) + ht) * 2 + kk)
+  const int kk = static_cast<int>(blk & 1);
+  const int64_t ht = (blk >> 1) % (h / 16);
+  const int64_t ks = (blk >> 1) / (h / 16);
+  const int64_t row = 16 * ht + (l & 15);
+  const int64_t col = 64 * ks + 32 * kk + 8 * (l >> 4);
+  *reinterpret_cast<u32x4*>(out + f * 8) = *reinterpret_cast<const u32x4*>(w1 + row * d + col);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one wave per row.  u = gamma*x/rms is formed on the fly;
 // lane j accumulates z_j over the row (x broadcast from L1), then the wave
 // reduces w2 . SiLU(z) across lanes.
@@ -352,62 +661,97 @@ void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint
     launch_bf16_f<TM, NT, false>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d);
 }
 
-}  // namespace
-}  // namespace tg
+// Streaming kernel dispatch: h = 16 * NTW * NW.
+void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
+                   const uint16_t* x, int64_t ld, const uint8_t* p, float eps,
+                   const uint16_t* w, const float* b1, const float* w2, float b2, float* out) {
+  const dim3 grid(static_cast<uint32_t>((T + 63) / 64));
+  const int32_t T32 = static_cast<int32_t>(T), h32 = static_cast<int32_t>(h);
+#define TG_GATE_STREAM(NTW, NW, NST)                                                         \
+  do {                                                                                      \
+    if (packed)                                                                             \
+      gate_bf16_stream_kernel<NTW, NW, NST, true><<<grid, dim3(NW * 64), 0, s>>>(           \
+          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32);                                  \
+    else                                                                                    \
+      gate_bf16_stream_kernel<NTW, NW, NST, false><<<grid, dim3(NW * 64), 0, s>>>(          \
+          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32);                                  \
+  } while (0)
+  if (h == 256 && d == 2048) TG_GATE_STREAM(2, 8, 32);   // Qwen3-1.7B hidden size, h = 256
+  else if (h == 256) TG_GATE_STREAM(2, 8, 0);
+  else if (h == 192) TG_GATE_STREAM(3, 4, 0);
+  else if (h == 128) TG_GATE_STREAM(2, 4, 0);
+  else TG_GATE_STREAM(1, 4, 0);
+#undef TG_GATE_STREAM
+}
 
-extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
-                                   const void* resid, int64_t resid_row_stride,
-                                   const uint8_t* prunable, const float* rms_weight, float eps,
-                                   const void* w1, const float* b1, const float* w2, float b2,
-                                   float* scores, void* stream) {
-  using namespace tg;
+tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                          const void* resid, int64_t resid_row_stride, const uint8_t* prunable,
+                          const float* rms_weight, float eps, const void* w1, bool packed,
+                          const float* b1, const float* w2, float b2, float* scores,
+                          void* stream) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: unknown dtype %d", (int)dt);
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dt);
   if (T < 0 || T > kMaxTokens || d < 1 || h < 1 || d > kMaxTokens || h > kMaxTokens)
     return fail(TG_ERR_INVALID_ARGUMENT,
-                "tg_gate_score: need 0 <= T <= 2^31-1, d >= 1, h >= 1 (T=%lld d=%lld h=%lld)",
+                "%s: need 0 <= T <= 2^31-1, d >= 1, h >= 1 (T=%lld d=%lld h=%lld)", fn,
                 (long long)T, (long long)d, (long long)h);
-  if (!(eps >= 0.0f))
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: eps must be >= 0");
+  if (!(eps >= 0.0f)) return fail(TG_ERR_INVALID_ARGUMENT, "%s: eps must be >= 0", fn);
+  if (packed) {
+    if (dt != TG_DTYPE_BF16)
+      return fail(TG_ERR_UNSUPPORTED, "%s: packed W1 is a bf16 layout", fn);
+    if (d % kKS != 0 || d < 2 * kKS || h % 64 != 0 || h > 256)
+      return fail(TG_ERR_UNSUPPORTED,
+                  "%s: packed W1 needs d %% 64 == 0, d >= 128, h in {64, 128, 192, 256} "
+                  "(d=%lld h=%lld)", fn, (long long)d, (long long)h);
+    if (rms_weight != nullptr)
+      return fail(TG_ERR_UNSUPPORTED,
+                  "%s: packed W1 takes no RMSNorm weight (pass NULL for a unit weight)", fn);
+  }
   if (T == 0) {
     clear_error();
     return TG_OK;
   }
   if (!resid || !prunable || !w1 || !w2 || !scores)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: NULL resid/prunable/w1/w2/scores");
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: NULL resid/prunable/w1/w2/scores", fn);
   if (resid_row_stride < d)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: resid_row_stride %lld < d %lld",
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: resid_row_stride %lld < d %lld", fn,
                 (long long)resid_row_stride, (long long)d);
   hipStream_t s = as_stream(stream);
   if (dt == TG_DTYPE_F32) {
     if (!aligned(resid, 4) || !aligned(w1, 4))
-      return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_score: misaligned f32 pointer");
+      return fail(TG_ERR_INVALID_ARGUMENT, "%s: misaligned f32 pointer", fn);
     const int64_t blocks = (T + 3) / 4;
     gate_f32_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
         static_cast<const float*>(resid), resid_row_stride, prunable, rms_weight, eps,
         static_cast<const float*>(w1), b1, w2, b2, scores, static_cast<int32_t>(T),
         static_cast<int32_t>(d), static_cast<int32_t>(h));
-    return check_launch("tg_gate_score");
+    return check_launch(fn);
   }
   if (d % 8 != 0)
-    return fail(TG_ERR_UNSUPPORTED, "tg_gate_score: bf16 path needs d %% 8 == 0 (d=%lld)",
-                (long long)d);
+    return fail(TG_ERR_UNSUPPORTED, "%s: bf16 path needs d %% 8 == 0 (d=%lld)", fn, (long long)d);
   if (h % 64 != 0 || h > 256)
-    return fail(TG_ERR_UNSUPPORTED,
-                "tg_gate_score: bf16 path needs h in {64, 128, 192, 256} (h=%lld)",
+    return fail(TG_ERR_UNSUPPORTED, "%s: bf16 path needs h in {64, 128, 192, 256} (h=%lld)", fn,
                 (long long)h);
   if (rms_weight != nullptr && d > 16384)
     return fail(TG_ERR_UNSUPPORTED,
-                "tg_gate_score: bf16 path with an RMSNorm weight needs d <= 16384 (LDS-staged)");
+                "%s: bf16 path with an RMSNorm weight needs d <= 16384 (LDS-staged)", fn);
   if (static_cast<int64_t>(TG_GATE_TM) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED,
-                "tg_gate_score: bf16 path addresses a 64-row tile and W1 with 31-bit offsets");
+                "%s: bf16 path addresses a 64-row tile and W1 with 31-bit offsets", fn);
   if (!aligned(resid, 16) || !aligned(w1, 16) || (resid_row_stride % 8) != 0)
     return fail(TG_ERR_INVALID_ARGUMENT,
-                "tg_gate_score: bf16 resid/w1 must be 16-byte aligned, row stride %% 8 == 0");
+                "%s: bf16 resid/w1 must be 16-byte aligned, row stride %% 8 == 0", fn);
   const auto* x = static_cast<const uint16_t*>(resid);
   const auto* w = static_cast<const uint16_t*>(w1);
   const int32_t d32 = static_cast<int32_t>(d);
+  if (packed) {
+    launch_stream(true, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores);
+    return check_launch(fn);
+  }
+  if (rms_weight == nullptr && d % kKS == 0 && d >= 2 * kKS) {
+    launch_stream(false, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores);
+    return check_launch(fn);
+  }
   const bool g = rms_weight != nullptr;
   constexpr int TM = TG_GATE_TM;
   const dim3 grid(static_cast<uint32_t>((T + TM - 1) / TM));
@@ -417,5 +761,57 @@ extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
     case 3: launch_bf16<TM, 3>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
     default: launch_bf16<TM, 4>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
   }
-  return check_launch("tg_gate_score");
+  return check_launch(fn);
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                                   const void* resid, int64_t resid_row_stride,
+                                   const uint8_t* prunable, const float* rms_weight, float eps,
+                                   const void* w1, const float* b1, const float* w2, float b2,
+                                   float* scores, void* stream) {
+  return tg::gate_score_impl("tg_gate_score", dt, T, d, h, resid, resid_row_stride, prunable,
+                             rms_weight, eps, w1, false, b1, w2, b2, scores, stream);
+}
+
+extern "C" tg_status tg_gate_score_packed(tg_dtype dt, int64_t T, int64_t d, int64_t h,
+                                          const void* resid, int64_t resid_row_stride,
+                                          const uint8_t* prunable, const float* rms_weight,
+                                          float eps, const void* w1_packed, const float* b1,
+                                          const float* w2, float b2, float* scores,
+                                          void* stream) {
+  return tg::gate_score_impl("tg_gate_score_packed", dt, T, d, h, resid, resid_row_stride,
+                             prunable, rms_weight, eps, w1_packed, true, b1, w2, b2, scores,
+                             stream);
+}
+
+extern "C" size_t tg_gate_w1_packed_bytes(tg_dtype dt, int64_t h, int64_t d) {
+  if (dt != TG_DTYPE_BF16 || h < 64 || h > 256 || h % 64 != 0 || d < 128 || d % 64 != 0 ||
+      d > tg::kMaxTokens)
+    return 0;
+  return static_cast<size_t>(h) * static_cast<size_t>(d) * 2u;
+}
+
+extern "C" tg_status tg_gate_pack_w1(tg_dtype dt, int64_t h, int64_t d, const void* w1,
+                                     void* w1_packed, void* stream) {
+  using namespace tg;
+  const size_t bytes = tg_gate_w1_packed_bytes(dt, h, d);
+  if (bytes == 0)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_gate_pack_w1: needs bf16, d %% 64 == 0, d >= 128, h in {64, 128, 192, 256} "
+                "(dt=%d h=%lld d=%lld)", (int)dt, (long long)h, (long long)d);
+  if (static_cast<int64_t>(bytes) > kMaxTokens)
+    return fail(TG_ERR_UNSUPPORTED, "tg_gate_pack_w1: W1 must stay below 2^31 bytes");
+  if (!w1 || !w1_packed)
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_pack_w1: NULL w1/w1_packed");
+  if (!aligned(w1, 16) || !aligned(w1_packed, 16))
+    return fail(TG_ERR_INVALID_ARGUMENT, "tg_gate_pack_w1: pointers must be 16-byte aligned");
+  const int64_t nfrag = static_cast<int64_t>(bytes / 16);
+  gate_pack_w1_kernel<<<dim3(static_cast<uint32_t>((nfrag + 255) / 256)), dim3(256), 0,
+                        as_stream(stream)>>>(static_cast<const uint16_t*>(w1),
+                                             static_cast<uint16_t*>(w1_packed),
+                                             static_cast<int32_t>(h), static_cast<int32_t>(d));
+  return check_launch("tg_gate_pack_w1");
 }

@@ -93,6 +93,32 @@ def test_gate_validation(lib):
     assert "d % 8" in lib.tg_last_error().decode() or True
 
 
+def test_gate_packed_validation(lib):
+    assert lib.tg_gate_w1_packed_bytes(BF16, 256, 2048) == 256 * 2048 * 2
+    assert lib.tg_gate_w1_packed_bytes(BF16, 64, 128) == 64 * 128 * 2
+    assert lib.tg_gate_w1_packed_bytes(F32, 256, 2048) == 0      # a bf16 layout
+    assert lib.tg_gate_w1_packed_bytes(BF16, 96, 2048) == 0      # h not a multiple of 64
+    assert lib.tg_gate_w1_packed_bytes(BF16, 256, 2000) == 0     # d % 64 != 0
+    assert lib.tg_gate_w1_packed_bytes(BF16, 256, 64) == 0       # d < 128
+    assert lib.tg_gate_pack_w1(BF16, 256, 2000, FAKE, FAKE, None) == UNSUP
+    assert lib.tg_gate_pack_w1(F32, 256, 2048, FAKE, FAKE, None) == UNSUP
+    assert lib.tg_gate_pack_w1(BF16, 256, 2048, None, FAKE, None) == INVAL
+    assert lib.tg_gate_pack_w1(BF16, 256, 2048, FAKE, None, None) == INVAL
+    assert lib.tg_gate_pack_w1(BF16, 256, 2048, FAKE_ODD, FAKE, None) == INVAL
+
+    def packed(dt=BF16, T=64, d=2048, h=256, gamma=None, w1=FAKE):
+        return lib.tg_gate_score_packed(dt, T, d, h, FAKE, d, FAKE, gamma,
+                                        ctypes.c_float(1e-6), w1, None, FAKE,
+                                        ctypes.c_float(0.0), FAKE, None)
+    assert packed(dt=F32) == UNSUP
+    assert packed(d=2000) == UNSUP
+    assert packed(h=96) == UNSUP
+    assert packed(gamma=FAKE) == UNSUP          # unit RMSNorm weight only
+    assert packed(w1=None) == INVAL
+    assert packed(T=0) == OK
+    assert "packed" in lib.tg_last_error().decode() or True
+
+
 def _select(lib, T=100, scores=FAKE, prunable=FAKE, K=10, kept=FAKE, cap=100, n_kept=FAKE,
             ws=FAKE, ws_bytes=None):
     if ws_bytes is None:
