@@ -349,6 +349,211 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
 
 __global__ void write_zero_kernel(int32_t* p) { p[0] = 0; }
 
+// ---------------------------------------------------------------------------
+// Single-workgroup path (T <= kLdsTokens): the whole selection in one launch.
+// Every token's key is staged once in LDS as key + 1 (0 marks a non-prunable
+// token; the largest key, +inf's, still fits), then the same three digit
+// passes and the same ordered compaction run out of LDS, with block-wide
+// scans instead of cross-workgroup counters.  The workspace is not touched.
+// ---------------------------------------------------------------------------
+constexpr int kLdsTokens = 32768;
+constexpr int kOneThreads = 1024;
+
+// Inclusive sum scan of one u32 per lane over the 64 lanes of a wave: four
+// row shifts (within rows of 16 lanes), then the row broadcasts 15 and 31
+// carry each row's total into the rows above it.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  int x = static_cast<int>(v);
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return static_cast<uint32_t>(x);
+}
+
+// Inclusive scan of a pair of u32 over the 1024 threads of the workgroup.
+__device__ __forceinline__ void wg_inclusive_scan2(uint32_t& a, uint32_t& b, uint32_t* s_wave,
+                                                   uint32_t& tot_a, uint32_t& tot_b) {
+  constexpr int NW = kOneThreads / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_inclusive_scan(a);
+  b = wave_inclusive_scan(b);
+  if (lane == 63) {
+    s_wave[wave] = a;
+    s_wave[NW + wave] = b;
+  }
+  __syncthreads();
+  uint32_t ba = 0, bb = 0, ta = 0, tb = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint32_t xa = s_wave[w], xb = s_wave[NW + w];
+    ba += w < wave ? xa : 0u;
+    bb += w < wave ? xb : 0u;
+    ta += xa;
+    tb += xb;
+  }
+  a += ba;
+  b += bb;
+  tot_a = ta;
+  tot_b = tb;
+}
+
+__global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
+    const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
+    uint32_t K, int32_t* __restrict__ kept_idx, int64_t capacity,
+    int32_t* __restrict__ n_kept) {
+  __shared__ __attribute__((aligned(16))) uint32_t keys[kLdsTokens];
+  __shared__ uint32_t hist[2048];
+  __shared__ uint32_t s_wave[2 * (kOneThreads / 64)];
+  __shared__ uint32_t s_state[4];   // prefix, mask, need, resolved
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+
+  for (int b = tid; b < 2048; b += kOneThreads) hist[b] = 0;
+  // staging: each thread takes 16 consecutive tokens per round with 16-byte
+  // buffer loads (all issued before any is used); past T they read zeros,
+  // i.e. non-prunable (the thread holding the tail reads its bytes singly)
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(prunable), 0, T, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scores), 0, T * 4, 0x00020000);
+  for (int base = 0; base < T; base += kOneThreads * 16) {
+    const int t0 = base + tid * 16;
+    if (t0 < T) {
+      u32x4 pm = __builtin_amdgcn_raw_buffer_load_b128(p_rs, t0, 0, 0);
+      u32x4 sv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(s_rs, (t0 + 4 * j) * 4, 0, 0);
+      if (t0 + 16 > T) {   // the range check is per dword: fetch the tail bytewise
+        pm = u32x4{0, 0, 0, 0};
+        for (int e = 0; t0 + e < T; ++e)
+          pm[e >> 2] |= static_cast<uint32_t>(prunable[t0 + e] != 0) << (8 * (e & 3));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 kv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool p = ((pm[j] >> (8 * e)) & 0xffu) != 0;
+          kv[e] = p ? score_key(__uint_as_float(sv[j][e])) + 1u : 0u;
+        }
+        // t0 + 15 < kLdsTokens: t0 is a multiple of 16 below T <= kLdsTokens
+        *reinterpret_cast<u32x4*>(&keys[t0 + 4 * j]) = kv;
+      }
+    }
+  }
+  __syncthreads();
+
+  // threshold: up to three digit passes; wave 0 resolves each digit
+  uint32_t prefix = 0, mask = 0, need = K;
+#pragma unroll
+  for (int pass = 0; pass < 3; ++pass) {
+    const int bits = pass == 2 ? 10 : 11;
+    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+    const uint32_t nb = 1u << bits;
+    if (pass > 0) {
+      for (uint32_t b = tid; b < nb; b += kOneThreads) hist[b] = 0;
+      __syncthreads();
+    }
+    for (int t = tid; t < T; t += kOneThreads) {
+      const uint32_t k = keys[t];
+      if (k != 0 && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys)
+      const int bpl = static_cast<int>(nb) / 64;
+      const int top = static_cast<int>(nb) - 1 - lane * bpl;
+      uint32_t mine = 0;
+      for (int j = 0; j < bpl; ++j) mine += hist[top - j];
+      const uint32_t incl = wave_inclusive_scan(mine);
+      const uint32_t total = __shfl(incl, 63, 64);
+      uint32_t nd = need;
+      if (pass == 0) {   // total = |P|: every prunable key matches the empty prefix
+        if (K >= total || K == 0) {
+          if (lane == 0) {
+            s_state[0] = 0;
+            s_state[1] = 0;
+            s_state[2] = K >= total ? total : 0u;
+            s_state[3] = 1;
+          }
+          nd = 0;   // no lane resolves a digit
+        }
+      }
+      const uint32_t above = incl - mine;
+      if (nd != 0 && above < nd && nd <= above + mine) {
+        uint32_t cum = above;
+        for (int j = 0; j < bpl; ++j) {
+          const int b = top - j;
+          const uint32_t c = hist[b];
+          if (cum + c >= nd) {
+            s_state[0] = prefix | (static_cast<uint32_t>(b) << shift);
+            s_state[1] = mask | ((nb - 1) << shift);
+            s_state[2] = nd - cum;
+            s_state[3] = (nd - cum == c || pass == 2) ? 1u : 0u;
+            break;
+          }
+          cum += c;
+        }
+      }
+    }
+    __syncthreads();
+    prefix = s_state[0];
+    mask = s_state[1];
+    need = s_state[2];
+    const bool resolved = s_state[3] != 0;
+    __syncthreads();   // s_state may be rewritten by the next pass
+    if (resolved) break;   // uniform across the workgroup
+  }
+
+  // ordered compaction: thread tid owns the contiguous tokens
+  // [tid * C, tid * C + C), C a multiple of 4; one workgroup scan of the
+  // counts (a, b) gives every thread its output slots
+  const int C = ((T + kOneThreads - 1) / kOneThreads + 3) & ~3;
+  const int c0 = tid * C;
+  uint32_t ca = 0, cb = 0;
+  for (int i = 0; i < C; i += 4) {
+    if (c0 + i < T) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[c0 + i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = kv[e];
+        const bool in = c0 + i + e < T;
+        const uint32_t km = k & mask;
+        ca += in && (k == 0 || km > prefix);
+        cb += in && k != 0 && km == prefix;
+      }
+    }
+  }
+  uint32_t xa = ca, xb = cb, tot_a = 0, tot_b = 0;
+  wg_inclusive_scan2(xa, xb, s_wave, tot_a, tot_b);
+  xa -= ca;   // exclusive prefixes
+  xb -= cb;
+  for (int i = 0; i < C; i += 4) {
+    if (c0 + i < T) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[c0 + i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = c0 + i + e;
+        const uint32_t k = kv[e];
+        const uint32_t km = k & mask;
+        const bool fa = t < T && (k == 0 || km > prefix);
+        const bool fb = t < T && k != 0 && km == prefix;
+        if (fa || (fb && xb < need)) {
+          const int64_t slot = static_cast<int64_t>(xa) + (xb < need ? xb : need);
+          if (slot < capacity) kept_idx[slot] = t;
+        }
+        xa += fa;
+        xb += fb;
+      }
+    }
+  }
+  if (tid == 0) n_kept[0] = static_cast<int32_t>(tot_a + (tot_b < need ? tot_b : need));
+}
+
 }  // namespace
 }  // namespace tg
 
@@ -393,9 +598,15 @@ extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_
   if (!aligned(workspace, 256))
     return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace must be 256-byte aligned");
 
+  const uint32_t Kc = static_cast<uint32_t>(K < T ? K : T);
+  if (T <= kLdsTokens && aligned(prunable, 16)) {
+    select_one_wg_kernel<<<dim3(1), dim3(kOneThreads), 0, s>>>(scores, prunable,
+                                                               static_cast<int32_t>(T), Kc,
+                                                               kept_idx, kept_capacity, n_kept);
+    return check_launch("tg_topk_select");
+  }
   int64_t per_block = 0;
   const int64_t G = blocks_for(T, &per_block);
-  const uint32_t Kc = static_cast<uint32_t>(K < T ? K : T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int32_t T32 = static_cast<int32_t>(T);
   radix_hist_kernel<0><<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block,
