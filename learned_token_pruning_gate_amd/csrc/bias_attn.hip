@@ -27,8 +27,17 @@
 //     matched by reading V^T from LDS in the same order.
 //   * Q stays in registers for the whole key loop.  K tiles are staged in
 //     LDS row-major (padded); V tiles are transposed on their way into LDS
-//     (4 keys x 8 dims per thread, packed with byte permutes).  The next
-//     tile's global loads are issued before the current tile's math.
+//     (4 keys x 8 dims per thread, packed with byte permutes), the keys of
+//     every 16-key PV step stored in the order the P^T accumulator holds
+//     them, so each lane's V^T operand is one 16-byte read.  The next tile's
+//     global loads are issued before the current tile's math.
+//   * The two 32-key halves of a tile's logits are independent accumulation
+//     chains, interleaved so no MFMA waits on its own predecessor.
+//   * Key streams: when the grid is small (short prompts, where the longest
+//     causal rows set the time), a workgroup runs two streams of 4 waves on
+//     the even and odd key tiles, each with its own LDS buffers, and merges
+//     their softmax states at the end; each wave's serial loop halves and
+//     two waves share every SIMD.
 //   * The bias gain_h*log2(e)*score_c is formed once per key tile and head
 //     in LDS; logits use exp2 with log2(e) folded into the scale; the output
 //     is rescaled only when some query's running max grows.
@@ -46,12 +55,17 @@ constexpr int kBK = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Slot of the 4-key group g (0..3) of a 16-key PV k-step in V^T: lane half
+// hh reads slots 8hh..8hh+7, which must hold keys 4hh..4hh+3 and 8+4hh..8+4hh+3
+// (the order the P^T accumulator holds them in).
+__device__ __forceinline__ int vgroup_slot(int g) { return ((g & 1) << 1) | (g >> 1); }
+
 template <int D>
 struct AttnSmem {
   static constexpr int KP = D + 8;          // K row pitch (bf16)
   static constexpr int VP = kBK + 8;        // V^T row pitch (bf16)
   uint16_t ks[kBK * KP];                    // K tile, row-major [key][dim]
-  uint16_t vt[D * VP];                      // V tile transposed [dim][key]
+  uint16_t vt[D * VP];                      // V tile transposed [dim][key slot]
   u32x2 bias[4][kBK];                       // per head: bf16 (hi | mid << 16, lo)
 };
 
@@ -83,8 +97,8 @@ __device__ __forceinline__ u32x2 split_bf16_triple(float v) {
   return u32x2{hi | (mid << 16), lo};
 }
 
-template <int D, int HPW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
+template <int D, int HPW, int KS, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
+__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
@@ -97,9 +111,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
   constexpr int KRPI = 256 / CPR;           // K rows staged per pass
   constexpr int KI = kBK / KRPI;            // K staging passes
   constexpr int VT = (kBK / 4) * CPR;       // threads that stage V
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[2];
+  // KS key streams: stream kh (waves 4kh .. 4kh+3, threads 256kh ..) takes
+  // key tiles kh, kh + KS, kh + 2KS, ... with its own LDS buffers; the
+  // streams' partial softmax states are merged at the end
+  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[2][KS];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x & 255;        // thread index within the key stream
+  const int kh = threadIdx.x >> 8;          // key stream
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
@@ -187,6 +205,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     for (int i = 0; i < KI; ++i)
       *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kreg[i];
     if (tid < VT) {
+      // keys 4 vkg .. 4 vkg + 3 go to the slots the PV k-step reads them from
+      const int vslot = 16 * (vkg >> 2) + 4 * vgroup_slot(vkg & 3);
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
         // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
@@ -195,8 +215,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
         lo[1] = pack_lo(vreg[2][w], vreg[3][w]);
         hi[0] = pack_hi(vreg[0][w], vreg[1][w]);
         hi[1] = pack_hi(vreg[2][w], vreg[3][w]);
-        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + 4 * vkg]) = lo;
-        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + 4 * vkg]) = hi;
+        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + vslot]) = lo;
+        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + vslot]) = hi;
       }
     }
     if (HAS_BIAS && tid < HPW * kBK)
@@ -212,30 +232,40 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float l_run = 0.0f;       // this lane's share of the running sum of 2^y
 
-  load_tile(0);
-  store_tile(sm[0]);
+  if (kh < n_tiles) {
+    load_tile(kh);
+    store_tile(sm[0][kh]);
+  }
   __syncthreads();
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const AttnSmem<D>& b = sm[t & 1];
+  const int n_rounds = (n_tiles + KS - 1) / KS;
+  for (int j = 0; j < n_rounds; ++j) {
+    const int t = KS * j + kh;               // this stream's tile
+    const AttnSmem<D>& b = sm[j & 1][kh];
     const int k0 = t * kBK;
-    const bool more = t + 1 < n_tiles;
-    if (more) load_tile(t + 1);
+    const bool more = t + KS < n_tiles;
+    if (more) load_tile(t + KS);
     // keep the next tile's loads issued here, ahead of this tile's math
     __builtin_amdgcn_sched_barrier(0);
+    if (KS == 1 || t < n_tiles) {   // uniform per wave: a stream may idle in the last round
 
-    // S'^T = K' Q'^T = <q, k> + bias'
+    // S'^T = K' Q'^T = <q, k> + bias'; the two 32-key halves are independent
+    // accumulation chains, interleaved so neither waits on its own last MFMA
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
-      const uint16_t* kp = &b.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh];
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * ks);
+    for (int ks = 0; ks < DK; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+            &b.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh + 16 * ks]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
       u32x4 ke = u32x4{0, 0, 0, 0};
       if (hh == 0) {
         const u32x2 bb = HAS_BIAS ? b.bias[hw][32 * kb + l32] : u32x2{0, 0};
@@ -297,26 +327,56 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(
           p[kb][hf][i] = static_cast<__bf16>(e);
         }
 
-    // O^T += V^T P^T: k-step (kb, hf) covers keys 32kb + 16hf + {4hh..4hh+3, 8+4hh..8+4hh+3}
+    // O^T += V^T P^T: k-step (kb, hf) covers keys 32kb + 16hf + {4hh..4hh+3,
+    // 8+4hh..8+4hh+3}, stored at slots 32kb + 16hf + 8hh .. +7: one 16-byte read
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int kcol = 32 * kb + 16 * hf + 4 * hh;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const uint16_t* vp = &b.vt[(32 * db + l32) * AttnSmem<D>::VP + kcol];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
-          const u32x4 a4 = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          const u32x4 a4 = *reinterpret_cast<const u32x4*>(
+              &b.vt[(32 * db + l32) * AttnSmem<D>::VP + 32 * kb + 16 * hf + 8 * hh]);
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
                                                           p[kb][hf], o[db], 0, 0, 0);
         }
       }
     }
 
-    if (more) store_tile(sm[(t + 1) & 1]);
+    }
+    if (more) store_tile(sm[(j + 1) & 1][kh]);
     __syncthreads();
+  }
+  if (KS > 1) {
+    // merge the streams' (running max, partial sums, O^T) into stream 0
+    constexpr int NV = DB * 16 + 2;
+    float* xch = reinterpret_cast<float*>(&sm[0][0]);
+    const int slot = wave * 64 + lane;
+    if (kh > 0) {
+      float* dst = xch + static_cast<size_t>((kh - 1) * 256 + slot) * NV;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[db * 16 + r] = o[db][r];
+      dst[DB * 16] = m_run;
+      dst[DB * 16 + 1] = l_run;
+    }
+    __syncthreads();
+    if (kh > 0) return;
+#pragma unroll
+    for (int other = 1; other < KS; ++other) {
+      const float* src = xch + static_cast<size_t>((other - 1) * 256 + slot) * NV;
+      const float m1 = src[DB * 16];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m);
+      const float a1 = m1 == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * a0 + src[db * 16 + r] * a1;
+      l_run = l_run * a0 + src[DB * 16 + 1] * a1;
+      m_run = m;
+    }
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -394,14 +454,19 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
   if (lse) lse[static_cast<int64_t>(h) * N + r] = l > 0.0f ? m + logf(l) : -INFINITY;
 }
 
-template <int D, int HPW, bool CAUSAL>
-void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
+// Two key streams per workgroup halve each wave's serial key loop, at the
+// cost of a whole CU's LDS per workgroup: they pay off while the grid is too
+// small to keep every CU busy with one-stream workgroups for several rounds.
+constexpr int64_t kTwoStreamMaxGrid = 1024;
+
+template <int D, int HPW, bool CAUSAL, int KS>
+void launch_bf16_attn_ks(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
                       const uint16_t* q, const uint16_t* k, const uint16_t* v,
                       const float* ks, const float* gain, const float* qs, float scale_log2,
                       uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
                       int32_t npb, int32_t nhg) {
 #define TG_ATTN_LAUNCH(B, Q)                                                         \
-  attn_bf16_kernel<D, HPW, CAUSAL, B, Q><<<grid, dim3(256), 0, s>>>(                \
+  attn_bf16_kernel<D, HPW, KS, CAUSAL, B, Q><<<grid, dim3(256 * KS), 0, s>>>(        \
       q, k, v, ks, gain, qs, scale_log2, out, lse, N, Hq, Hkv, npb, nhg)
   if (has_bias) {
     if (has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
@@ -409,6 +474,20 @@ void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
     if (has_qs) TG_ATTN_LAUNCH(false, true); else TG_ATTN_LAUNCH(false, false);
   }
 #undef TG_ATTN_LAUNCH
+}
+
+template <int D, int HPW, bool CAUSAL>
+void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
+                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                      const float* ks, const float* gain, const float* qs, float scale_log2,
+                      uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
+                      int32_t npb, int32_t nhg) {
+  if (static_cast<int64_t>(grid.x) <= kTwoStreamMaxGrid)
+    launch_bf16_attn_ks<D, HPW, CAUSAL, 2>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
+                                           scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+  else
+    launch_bf16_attn_ks<D, HPW, CAUSAL, 1>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
+                                           scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
 }
 
 template <int D, int HPW>
