@@ -8,6 +8,11 @@ before the timed region; outputs are preallocated.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t16k]
 
+By default each timed step is one replay of the four calls captured as a HIP
+graph (tg_chain_create); --mode eager launches them one by one.  Per-stage
+times come from HIP events around each call of an eager run of the same
+steps.
+
 Prints one JSON line: tokens/s for the whole step, per-stage event timings,
 the roofline of the dominant kernel, and the CPU oracle timed on a bounded
 sample of the same workload (a reported baseline, not the target).
@@ -130,6 +135,11 @@ def main():
                     help="gate W1 layout: packed once before timing (tg_gate_pack_w1, the "
                          "weight-load step) or row-major [h, d]; packed needs bf16 and a "
                          "unit RMSNorm weight")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="how the timed steps are launched: one replay of the chain "
+                         "captured as a HIP graph (tg_chain_create, the pages' serving "
+                         "recipe) per step, or the four calls launched one by one; "
+                         "the per-stage events always come from an eager run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel that "
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -254,8 +264,28 @@ def main():
 
     per_stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
                     for j, s in enumerate(stages)}
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = w.T * args.steps / elapsed
+    eager_ms = elapsed * 1e3 / args.steps
+
+    graph_ms = None
+    if args.mode == "graph":
+        chain = tg.tg_chain_create(
+            resid=resid, prunable=prunable, w1=w1, w2=w2, b1=b1, eps=g.eps, b2=g.b2,
+            w1_packed=use_packed, rms_weight=gamma if args.rms_weight else None,
+            scores=scores, K=w.K, kept_idx=kept, n_kept=n_kept, workspace=ws, N=N,
+            resid_kept=resid_kept, pos_kept=pos_kept, score_kept=score_kept, q=q, k=k, v=v,
+            attn_key_score=drawn if drawn is not None else score_kept, gain=gain,
+            q_scale=q_scale, out=out, lse=lse)
+        for _ in range(max(args.warmup, 1)):
+            chain.launch(stream)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            chain.launch(stream)
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        chain.close()
+    ms_per_step = graph_ms if graph_ms is not None else eager_ms
+    value = w.T / (ms_per_step * 1e-3)
 
     alg = algorithmic(w, N)
     stage_info = {}
@@ -303,6 +333,9 @@ def main():
                    "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
                    "gate_w1": "packed" if use_packed else "row-major",
                    "parallelism": "single-gpu"},
+        "mode": args.mode,
+        "eager_ms_per_step": eager_ms,
+        "graph_ms_per_step": graph_ms,
         "attn_tflops": stage_info["attn"].get("TFLOP_s"),
         "attn_frac_of_peak": stage_info["attn"].get("mfma_frac"),
         "roofline": roof,

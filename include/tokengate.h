@@ -18,6 +18,7 @@
  *   tg_topk_select     top-K selection and ordered compaction        [a2,a3]
  *   tg_compact_gather  gather of residual rows/positions/scores      [a4]
  *   tg_bias_attn_fwd   causal GQA attention with the gate bias       [a5]
+ *   tg_chain_*         the four calls captured as one HIP graph
  *
  * Conventions shared by every call
  * --------------------------------
@@ -228,6 +229,77 @@ tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
                            const float* gain, const float* q_scale,
                            float softmax_scale, int causal, void* out,
                            float* lse, void* stream);
+
+/* --------------------------------------------------------------------------
+ * The four calls captured once as a HIP graph and replayed.  Pages: ai.info
+ * summary "Key Contributions" item 4 (the serving recipe captures the pruned
+ * forward pass as a graph, so the short kernels of a small budget are not
+ * paced by launches).  The four calls above enqueue only kernels and never
+ * synchronise, so they are capturable as they stand.
+ *
+ * tg_chain_desc holds the arguments of the four calls, field for field as
+ * documented above (w1_packed selects tg_gate_score_packed; attn_key_score
+ * is the attention's key_score, normally score_kept).  tg_chain_create
+ * validates them through the calls themselves (a failing call's status and
+ * tg_last_error() come back unchanged and nothing is captured), captures the
+ * chain on an internal stream and instantiates it.  The graph keeps the
+ * pointers: the caller keeps every buffer alive and refills inputs in place.
+ * tg_chain_launch enqueues one replay on `stream`; replays on one stream are
+ * ordered and may not overlap a replay of the same chain on another stream
+ * (they share the workspace and outputs).  tg_chain_destroy frees the graph
+ * (NULL is a no-op).  Creating a chain allocates the runtime's graph objects
+ * (host memory and whatever the runtime keeps per graph); replays allocate
+ * nothing.
+ * ------------------------------------------------------------------------ */
+typedef struct tg_chain tg_chain;
+
+typedef struct tg_chain_desc {
+  /* tg_gate_score / tg_gate_score_packed */
+  tg_dtype dt;
+  int64_t T, d, h;
+  const void* resid;
+  int64_t resid_row_stride;
+  const uint8_t* prunable;
+  const float* rms_weight;
+  float eps;
+  const void* w1;
+  int w1_packed;
+  const float* b1;
+  const float* w2;
+  float b2;
+  float* scores;
+  /* tg_topk_select */
+  int64_t K;
+  int32_t* kept_idx;
+  int64_t kept_capacity;
+  int32_t* n_kept;
+  void* workspace;
+  size_t workspace_bytes;
+  /* tg_compact_gather */
+  int64_t N;
+  void* resid_kept;
+  int64_t kept_row_stride;
+  int32_t* pos_kept;
+  float* score_kept;
+  /* tg_bias_attn_fwd */
+  int64_t Hq, Hkv, D;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* attn_key_score;
+  const float* gain;
+  const float* q_scale;
+  float softmax_scale;
+  int causal;
+  void* out;
+  float* lse;
+} tg_chain_desc;
+
+tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain);
+
+tg_status tg_chain_launch(const tg_chain* chain, void* stream);
+
+void tg_chain_destroy(tg_chain* chain);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
 * ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
 * ``tg_compact_gather``   -- gather of rows, positions and scores
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
+* ``tg_chain_create`` / ``TgChain.launch`` -- the four calls captured once as
+                          a HIP graph and replayed
 """
 from __future__ import annotations
 
@@ -27,7 +29,7 @@ __all__ = [
     "TokenGateError", "lib_path", "load", "kept_count",
     "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
     "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
+    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_chain_create", "TgChain",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
     "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
 ]
@@ -40,7 +42,8 @@ TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
             "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd")
+            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_chain_create",
+            "tg_chain_launch", "tg_chain_destroy")
 
 
 class TokenGateError(RuntimeError):
@@ -50,6 +53,23 @@ class TokenGateError(RuntimeError):
 
 
 _lib = None
+
+
+class ChainDesc(ctypes.Structure):
+    """Mirror of tg_chain_desc (include/tokengate.h), field for field."""
+    _P, _I64, _F, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+    _fields_ = [
+        ("dt", _I), ("T", _I64), ("d", _I64), ("h", _I64), ("resid", _P),
+        ("resid_row_stride", _I64), ("prunable", _P), ("rms_weight", _P), ("eps", _F),
+        ("w1", _P), ("w1_packed", _I), ("b1", _P), ("w2", _P), ("b2", _F), ("scores", _P),
+        ("K", _I64), ("kept_idx", _P), ("kept_capacity", _I64), ("n_kept", _P),
+        ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+        ("N", _I64), ("resid_kept", _P), ("kept_row_stride", _I64), ("pos_kept", _P),
+        ("score_kept", _P),
+        ("Hq", _I64), ("Hkv", _I64), ("D", _I64), ("q", _P), ("k", _P), ("v", _P),
+        ("attn_key_score", _P), ("gain", _P), ("q_scale", _P), ("softmax_scale", _F),
+        ("causal", _I), ("out", _P), ("lse", _P),
+    ]
 
 
 def load():
@@ -83,6 +103,12 @@ def load():
     lib.tg_compact_gather.restype = I
     lib.tg_bias_attn_fwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P]
     lib.tg_bias_attn_fwd.restype = I
+    lib.tg_chain_create.argtypes = [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]
+    lib.tg_chain_create.restype = I
+    lib.tg_chain_launch.argtypes = [P, P]
+    lib.tg_chain_launch.restype = I
+    lib.tg_chain_destroy.argtypes = [P]
+    lib.tg_chain_destroy.restype = None
     _lib = lib
     return lib
 
@@ -120,6 +146,10 @@ def _dev(t, name, dtype=None, allow_none=False):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _addr(t):
+    return 0 if t is None else int(t.data_ptr())
 
 
 def _stream(stream):
@@ -214,6 +244,60 @@ def tg_gate_score_packed(resid, prunable, w1_packed, w2, b2=0.0, b1=None, eps=1e
                                   _ptr(w2), float(b2), _ptr(scores), _stream(stream))
     _check(st, "tg_gate_score_packed")
     return scores
+
+
+class TgChain:
+    """A captured chain (tg_chain_create); keeps its tensors alive."""
+
+    def __init__(self, handle, keep):
+        self._h = handle
+        self._keep = keep
+
+    def launch(self, stream=None):
+        if self._h is None:
+            raise ValueError("chain was closed")
+        _check(load().tg_chain_launch(self._h, _stream(stream)), "tg_chain_launch")
+
+    def close(self):
+        if self._h is not None:
+            load().tg_chain_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, workspace,
+                    N, resid_kept, pos_kept, score_kept, q, k, v, attn_key_score, gain,
+                    out, w1_packed=False, b2=0.0, rms_weight=None, b1=None, eps=1e-6,
+                    q_scale=None, softmax_scale=0.0, causal=True, lse=None):
+    """Capture gate -> top-K -> gather -> bias attention into one HIP graph.
+    Every argument is the tensor the corresponding call would take; the graph
+    keeps their addresses, so refill inputs in place between launches."""
+    lib = load()
+    T, d = resid.shape
+    h = w2.shape[0]
+    Nq, Hq, D = q.shape
+    desc = ChainDesc(
+        dt=_dt(resid), T=T, d=d, h=h, resid=_addr(resid), resid_row_stride=resid.stride(0),
+        prunable=_addr(prunable), rms_weight=_addr(rms_weight), eps=float(eps), w1=_addr(w1),
+        w1_packed=1 if w1_packed else 0, b1=_addr(b1), w2=_addr(w2), b2=float(b2),
+        scores=_addr(scores), K=int(K), kept_idx=_addr(kept_idx), kept_capacity=kept_idx.numel(),
+        n_kept=_addr(n_kept), workspace=_addr(workspace), workspace_bytes=workspace.numel(),
+        N=int(N), resid_kept=_addr(resid_kept), kept_row_stride=resid_kept.stride(0),
+        pos_kept=_addr(pos_kept), score_kept=_addr(score_kept), Hq=Hq, Hkv=k.shape[1], D=D,
+        q=_addr(q), k=_addr(k), v=_addr(v), attn_key_score=_addr(attn_key_score), gain=_addr(gain),
+        q_scale=_addr(q_scale), softmax_scale=float(softmax_scale), causal=1 if causal else 0,
+        out=_addr(out), lse=_addr(lse))
+    h_out = ctypes.c_void_p()
+    _check(lib.tg_chain_create(ctypes.byref(desc), ctypes.byref(h_out)), "tg_chain_create")
+    keep = [resid, prunable, w1, w2, scores, kept_idx, n_kept, workspace, resid_kept,
+            pos_kept, score_kept, q, k, v, attn_key_score, gain, out, rms_weight, b1,
+            q_scale, lse]
+    return TgChain(h_out, keep)
 
 
 def tg_topk_workspace_size(T: int) -> int:

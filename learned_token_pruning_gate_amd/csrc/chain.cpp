@@ -1,0 +1,95 @@
+// chain.cpp -- the four calls of the path captured once as a HIP graph and
+// replayed (TokenGate pages: ai.info summary "Key Contributions" item 4, the
+// graph-captured serving recipe).  Host code only: the capture records the
+// kernels that the four entry points enqueue; nothing here runs on the GPU
+// by itself.
+#include <new>
+
+#include "tg_common.hpp"
+
+struct tg_chain {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+tg_status run_chain(const tg_chain_desc& d, hipStream_t s) {
+  tg_status st =
+      d.w1_packed
+          ? tg_gate_score_packed(d.dt, d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
+                                 d.rms_weight, d.eps, d.w1, d.b1, d.w2, d.b2, d.scores, s)
+          : tg_gate_score(d.dt, d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
+                          d.rms_weight, d.eps, d.w1, d.b1, d.w2, d.b2, d.scores, s);
+  if (st != TG_OK) return st;
+  st = tg_topk_select(d.T, d.scores, d.prunable, d.K, d.kept_idx, d.kept_capacity, d.n_kept,
+                      d.workspace, d.workspace_bytes, s);
+  if (st != TG_OK) return st;
+  st = tg_compact_gather(d.dt, d.T, d.N, d.d, d.resid, d.resid_row_stride, d.scores,
+                         d.kept_idx, d.resid_kept, d.kept_row_stride, d.pos_kept, d.score_kept,
+                         s);
+  if (st != TG_OK) return st;
+  return tg_bias_attn_fwd(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score, d.gain,
+                          d.q_scale, d.softmax_scale, d.causal, d.out, d.lse, s);
+}
+
+}  // namespace
+
+extern "C" tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain) {
+  using namespace tg;
+  if (chain == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "tg_chain_create: chain is NULL");
+  *chain = nullptr;
+  if (desc == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "tg_chain_create: desc is NULL");
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess)
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: stream creation failed: %s", hipGetErrorString(e));
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: capture failed to begin: %s",
+                hipGetErrorString(e));
+  }
+  const tg_status st = run_chain(*desc, cs);
+  hipGraph_t graph = nullptr;
+  e = hipStreamEndCapture(cs, &graph);
+  (void)hipStreamDestroy(cs);
+  if (st != TG_OK) {   // the failing call's message is kept
+    if (graph) (void)hipGraphDestroy(graph);
+    return st;
+  }
+  if (e != hipSuccess || graph == nullptr)
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: capture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: instantiation failed: %s", hipGetErrorString(e));
+  }
+  tg_chain* c = new (std::nothrow) tg_chain{graph, exec};
+  if (c == nullptr) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: out of host memory");
+  }
+  *chain = c;
+  clear_error();
+  return TG_OK;
+}
+
+extern "C" tg_status tg_chain_launch(const tg_chain* chain, void* stream) {
+  using namespace tg;
+  if (chain == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "tg_chain_launch: chain is NULL");
+  const hipError_t e = hipGraphLaunch(chain->exec, as_stream(stream));
+  if (e != hipSuccess)
+    return fail(TG_ERR_LAUNCH, "tg_chain_launch: %s", hipGetErrorString(e));
+  clear_error();
+  return TG_OK;
+}
+
+extern "C" void tg_chain_destroy(tg_chain* chain) {
+  if (chain == nullptr) return;
+  (void)hipGraphExecDestroy(chain->exec);
+  (void)hipGraphDestroy(chain->graph);
+  delete chain;
+}

@@ -200,3 +200,33 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "tg_oracle" not in text, f
                 assert "liboracle" not in text, f
+
+
+def test_chain_null_arguments(lib):
+    """tg_chain_create validates its own pointers before any HIP call."""
+    import learned_token_pruning_gate_amd as tg
+    h = ctypes.c_void_p()
+    desc = tg.ChainDesc()
+    assert lib.tg_chain_create(None, ctypes.byref(h)) == INVAL
+    assert lib.tg_chain_create(ctypes.byref(desc), None) == INVAL
+    assert lib.tg_chain_launch(None, None) == INVAL
+    lib.tg_chain_destroy(None)          # a no-op
+
+
+def test_chain_desc_layout_matches_header():
+    """The ctypes mirror names the header's fields in the header's order."""
+    import learned_token_pruning_gate_amd as tg
+    src = open(HEADER).read()
+    body = src[src.index("typedef struct tg_chain_desc {"):src.index("} tg_chain_desc;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = []
+    for decl in body.split(";")[:-1]:
+        decl = decl.split("{")[-1].strip()
+        if not decl:
+            continue
+        # "int64_t T, d, h" -> T, d, h ; "const void* resid" -> resid
+        parts = decl.replace("*", " ").split(",")
+        first = parts[0].split()[-1]
+        names.append(first)
+        names.extend(p.strip() for p in parts[1:])
+    assert [f[0] for f in tg.ChainDesc._fields_] == names

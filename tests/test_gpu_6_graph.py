@@ -1,0 +1,120 @@
+"""The four calls captured as one HIP graph (tg_chain_create / launch): every
+replay must reproduce the eager chain bit for bit, also after the inputs are
+refilled in place and with eager work and synchronisation between replays.
+(TokenGate pages: ai.info summary "Key Contributions" item 4, the graph-
+captured serving recipe.)"""
+import numpy as np
+import pytest
+import torch
+
+import learned_token_pruning_gate_amd as tg
+import workloads
+from dataclasses import replace
+from gpu_util import report, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def make_case(w, packed):
+    g, a = workloads.generate(w)
+    dt = w.dtype
+    c = dict(resid=to_dev(g.resid, dt), prunable=to_dev(g.prunable), w2=to_dev(g.w2),
+             b1=to_dev(g.b1), q=to_dev(a.q, dt), k=to_dev(a.k, dt), v=to_dev(a.v, dt),
+             gain=to_dev(a.gain))
+    w1 = to_dev(g.w1, dt)
+    c["w1"] = tg.tg_gate_pack_w1(w1) if packed else w1
+    N, dev = w.n_kept, c["resid"].device
+    c.update(scores=torch.empty(w.T, dtype=torch.float32, device=dev),
+             kept_idx=torch.empty(w.T, dtype=torch.int32, device=dev),
+             n_kept=torch.empty(1, dtype=torch.int32, device=dev),
+             workspace=torch.zeros(tg.tg_topk_workspace_size(w.T), dtype=torch.uint8, device=dev),
+             resid_kept=torch.empty((N, w.d), dtype=c["resid"].dtype, device=dev),
+             pos_kept=torch.empty(N, dtype=torch.int32, device=dev),
+             score_kept=torch.empty(N, dtype=torch.float32, device=dev),
+             out=torch.empty_like(c["q"]),
+             lse=torch.empty((w.Hq, N), dtype=torch.float32, device=dev))
+    return c
+
+
+OUTS = ("scores", "kept_idx", "n_kept", "resid_kept", "pos_kept", "score_kept", "out", "lse")
+
+
+def eager(c, w, packed):
+    if packed:
+        tg.tg_gate_score_packed(c["resid"], c["prunable"], c["w1"], c["w2"], b1=c["b1"],
+                                eps=w.eps, scores=c["scores"])
+    else:
+        tg.tg_gate_score(c["resid"], c["prunable"], c["w1"], c["w2"], b1=c["b1"], eps=w.eps,
+                         scores=c["scores"])
+    tg.tg_topk_select(c["scores"], c["prunable"], w.K, kept_idx=c["kept_idx"],
+                      n_kept=c["n_kept"], workspace=c["workspace"])
+    tg.tg_compact_gather(c["resid"], c["scores"], c["kept_idx"], w.n_kept,
+                         resid_kept=c["resid_kept"], pos_kept=c["pos_kept"],
+                         score_kept=c["score_kept"])
+    tg.tg_bias_attn_fwd(c["q"], c["k"], c["v"], c["score_kept"], c["gain"], out=c["out"],
+                        lse=c["lse"])
+    torch.cuda.synchronize()
+    return {n: c[n].clone() for n in OUTS}
+
+
+def clobber(c):
+    for n in OUTS:
+        if c[n].dtype in (torch.float32, torch.bfloat16):
+            c[n].fill_(float("nan"))
+        else:
+            c[n].fill_(-7)
+
+
+def same(c, ref, what):
+    for n in OUTS:
+        a, b = c[n], ref[n]
+        if n == "kept_idx":   # entries past the kept count are unspecified
+            k = int(ref["n_kept"].item())
+            a, b = a[:k], b[:k]
+        assert torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                           b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), (what, n)
+
+
+CASES = [
+    ("tiny", False),
+    ("t16k", True),
+    ("t16k", False),
+    ("multi", True),   # T > 32768: the multi-workgroup top-K and its workspace
+]
+
+
+@pytest.mark.parametrize("name,packed", CASES)
+def test_graph_replays_match_eager(name, packed):
+    if name == "multi":
+        w = replace(workloads.get("t16k"), name="graph-40k", seed=11, T=40000, d=512, h=128,
+                    p_lo=100, p_hi=39900, K=700)
+    else:
+        w = workloads.get(name)
+    c = make_case(w, packed)
+    ref = eager(c, w, packed)
+    chain = tg.tg_chain_create(
+        resid=c["resid"], prunable=c["prunable"], w1=c["w1"], w2=c["w2"], b1=c["b1"],
+        eps=w.eps, w1_packed=packed, scores=c["scores"], K=w.K, kept_idx=c["kept_idx"],
+        n_kept=c["n_kept"], workspace=c["workspace"], N=w.n_kept, resid_kept=c["resid_kept"],
+        pos_kept=c["pos_kept"], score_kept=c["score_kept"], q=c["q"], k=c["k"], v=c["v"],
+        attn_key_score=c["score_kept"], gain=c["gain"], out=c["out"], lse=c["lse"])
+    for rep in range(3):
+        clobber(c)                     # eager work between replays
+        torch.cuda.synchronize()
+        chain.launch()
+        torch.cuda.synchronize()
+        same(c, ref, "%s replay %d" % (name, rep))
+    # refill the inputs in place: the graph reads the new values
+    gen = torch.Generator(device=c["resid"].device).manual_seed(5)
+    c["resid"].copy_(torch.randn(c["resid"].shape, generator=gen, device=c["resid"].device)
+                     .to(c["resid"].dtype))
+    c["q"].mul_(0.5)
+    ref2 = eager(c, w, packed)
+    clobber(c)
+    torch.cuda.synchronize()
+    chain.launch()
+    chain.launch()                     # two replays in a row on one stream
+    torch.cuda.synchronize()
+    same(c, ref2, name + " refilled")
+    chain.close()
+    report("graph_chain_" + name, packed=packed, replays=5, bit_exact=True)
