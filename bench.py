@@ -46,13 +46,14 @@ def source_sha(stage: str) -> str:
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
 
 
-def algorithmic(w, N):
+def algorithmic(w, N, kv_layers=0):
     """Per-launch algorithmic bytes and flops of each stage (what the method
     must move or compute, not what a kernel happens to touch)."""
     b = 2 if w.dtype == "bf16" else 4
     nP, T, d, h = w.n_prunable, w.T, w.d, w.h
     D, Hq, Hkv = w.D, w.Hq, w.Hkv
     return {
+        "kv": dict(bytes=2 * 2 * kv_layers * N * Hkv * D * b + 4 * N, flops=0),
         "gate": dict(bytes=nP * d * b + T + 4 * T + h * d * b, flops=2 * nP * d * h),
         "select": dict(bytes=4 * nP + T + 4 * N, flops=0),
         "gather": dict(bytes=2 * N * d * b + 16 * N, flops=0),
@@ -135,6 +136,10 @@ def main():
                     help="gate W1 layout: packed once before timing (tg_gate_pack_w1, the "
                          "weight-load step) or row-major [h, d]; packed needs bf16 and a "
                          "unit RMSNorm weight")
+    ap.add_argument("--kv-layers", type=int, default=0,
+                    help="also gather this many lower layers' K/V cache [L, T, Hkv, D] to "
+                         "the kept tokens (tg_kv_gather) on a second stream beside the "
+                         "attention; 0 (default) times the path without it")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="how the timed steps are launched: one replay of the chain "
                          "captured as a HIP graph (tg_chain_create, the pages' serving "
@@ -222,6 +227,16 @@ def main():
                                                      tg.tg_last_error()))
 
     stages = ["gate", "select", "gather", "attn"]
+    kvl = args.kv_layers
+    if kvl > 0:
+        kv_k = torch.randn((kvl, w.T, w.Hkv, w.D), device=dev).to(q.dtype)
+        kv_v = torch.randn((kvl, w.T, w.Hkv, w.D), device=dev).to(q.dtype)
+        kv_ko = torch.empty((kvl, N, w.Hkv, w.D), dtype=q.dtype, device=dev)
+        kv_vo = torch.empty_like(kv_ko)
+        kv_args = (dtc, kvl, w.T, N, w.Hkv, w.D, P(kv_k), P(kv_v), P(kept), P(kv_ko), P(kv_vo))
+        side = torch.cuda.Stream(device=dev)      # default priority
+        side_p = ctypes.c_void_p(side.cuda_stream)
+        fork_ev, join_ev = torch.cuda.Event(), torch.cuda.Event()
 
     gate_fn = lib.tg_gate_score_packed if use_packed else lib.tg_gate_score
 
@@ -237,9 +252,20 @@ def main():
         check(lib.tg_compact_gather(*gat_args), "tg_compact_gather")
         if ev is not None:
             ev[3].record(stream)
+        if kvl > 0:   # lower layers' KV gather on the side stream, beside the attention
+            fork_ev.record(stream)
+            side.wait_event(fork_ev)
+            if ev is not None:
+                ev[5].record(side)
+            check(lib.tg_kv_gather(*kv_args, side_p), "tg_kv_gather")
+            if ev is not None:
+                ev[6].record(side)
+            join_ev.record(side)
         check(lib.tg_bias_attn_fwd(*att_args), "tg_bias_attn_fwd")
         if ev is not None:
             ev[4].record(stream)
+        if kvl > 0:
+            stream.wait_event(join_ev)
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
@@ -253,7 +279,7 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(7)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -264,6 +290,8 @@ def main():
 
     per_stage_ms = {s: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in events]))
                     for j, s in enumerate(stages)}
+    if kvl > 0:
+        per_stage_ms["kv"] = float(np.mean([e[5].elapsed_time(e[6]) for e in events]))
     eager_ms = elapsed * 1e3 / args.steps
 
     graph_ms = None
@@ -274,7 +302,9 @@ def main():
             scores=scores, K=w.K, kept_idx=kept, n_kept=n_kept, workspace=ws, N=N,
             resid_kept=resid_kept, pos_kept=pos_kept, score_kept=score_kept, q=q, k=k, v=v,
             attn_key_score=drawn if drawn is not None else score_kept, gain=gain,
-            q_scale=q_scale, out=out, lse=lse)
+            q_scale=q_scale, out=out, lse=lse,
+            **(dict(kv_k_cache=kv_k, kv_v_cache=kv_v, kv_k_kept=kv_ko, kv_v_kept=kv_vo)
+               if kvl > 0 else {}))
         for _ in range(max(args.warmup, 1)):
             chain.launch(stream)
         torch.cuda.synchronize()
@@ -287,9 +317,9 @@ def main():
     ms_per_step = graph_ms if graph_ms is not None else eager_ms
     value = w.T / (ms_per_step * 1e-3)
 
-    alg = algorithmic(w, N)
+    alg = algorithmic(w, N, kvl)
     stage_info = {}
-    for s in stages:
+    for s in stages + (["kv"] if kvl > 0 else []):
         t = per_stage_ms[s] * 1e-3
         info = {"ms": per_stage_ms[s], "bytes": alg[s]["bytes"],
                 "GB_s": alg[s]["bytes"] / t / 1e9,
@@ -314,7 +344,7 @@ def main():
     cold = None
     if args.cold:
         flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)  # 512 MiB > MALL
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(10)]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(10)]
         for e in ev:
             flush.fill_(1)
             step(e)
@@ -332,6 +362,7 @@ def main():
                    "n_prunable": w.n_prunable, "K": w.K, "N_kept": N, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
                    "gate_w1": "packed" if use_packed else "row-major",
+                   "kv_layers": kvl,
                    "parallelism": "single-gpu"},
         "mode": args.mode,
         "eager_ms_per_step": eager_ms,

@@ -18,6 +18,7 @@
  *   tg_topk_select     top-K selection and ordered compaction        [a2,a3]
  *   tg_compact_gather  gather of residual rows/positions/scores      [a4]
  *   tg_bias_attn_fwd   causal GQA attention with the gate bias       [a5]
+ *   tg_kv_gather       lower layers' KV cache gathered to kept tokens
  *   tg_chain_*         the four calls captured as one HIP graph
  *
  * Conventions shared by every call
@@ -231,6 +232,31 @@ tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
                            float* lse, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Lower layers' KV cache gathered to the kept tokens.  Pages: ai.info summary
+ * "Key Contributions" item 1 (layers above the gate never create KV entries
+ * for pruned tokens) and "Methodology in Plain English" (the layers below
+ * the gate ran on every token): compacting the lower layers' cache with the
+ * same kept_idx leaves the prompt's whole KV cache holding kept tokens only.
+ *
+ *   k_kept[l][r] = k_cache[l][kept_idx[r]],  v_kept[l][r] = v_cache[l][kept_idx[r]]
+ *
+ * dt        dtype of the caches (bit copy; any dtype of that size works).
+ * L, T, N   lower layers, prompt tokens, kept tokens (L, T, N >= 0).
+ * Hkv, D    KV heads and head dim; Hkv * D * element size % 16 == 0.
+ * k_cache, v_cache  [L][T][Hkv][D] contiguous, 16-byte aligned; either may
+ *           be NULL together with its output (that tensor is skipped).
+ * kept_idx  [N] int32, as written by tg_topk_select.  An index outside
+ *           [0, T) yields a zero row.
+ * k_kept, v_kept    out, [L][N][Hkv][D] contiguous, 16-byte aligned.
+ * Enqueued on `stream`; meant for a second stream that waits for
+ * tg_topk_select and runs beside tg_bias_attn_fwd.
+ * ------------------------------------------------------------------------ */
+tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv,
+                       int64_t D, const void* k_cache, const void* v_cache,
+                       const int32_t* kept_idx, void* k_kept, void* v_kept,
+                       void* stream);
+
+/* --------------------------------------------------------------------------
  * The four calls captured once as a HIP graph and replayed.  Pages: ai.info
  * summary "Key Contributions" item 4 (the serving recipe captures the pruned
  * forward pass as a graph, so the short kernels of a small budget are not
@@ -239,7 +265,8 @@ tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
  *
  * tg_chain_desc holds the arguments of the four calls, field for field as
  * documented above (w1_packed selects tg_gate_score_packed; attn_key_score
- * is the attention's key_score, normally score_kept).  tg_chain_create
+ * is the attention's key_score, normally score_kept; the kv_ fields, if
+ * kv_L > 0, add tg_kv_gather with the desc's T, N, Hkv, D and kept_idx).  tg_chain_create
  * validates them through the calls themselves (a failing call's status and
  * tg_last_error() come back unchanged and nothing is captured), captures the
  * chain on an internal stream and instantiates it.  The graph keeps the
@@ -293,6 +320,14 @@ typedef struct tg_chain_desc {
   int causal;
   void* out;
   float* lse;
+  /* optional tg_kv_gather of kv_L lower layers (0: none), captured on a
+   * second stream that forks after tg_compact_gather and joins after
+   * tg_bias_attn_fwd, so the two run side by side in every replay */
+  int64_t kv_L;
+  const void* kv_k_cache;
+  const void* kv_v_cache;
+  void* kv_k_kept;
+  void* kv_v_kept;
 } tg_chain_desc;
 
 tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain);

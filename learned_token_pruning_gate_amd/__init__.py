@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
 * ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
 * ``tg_compact_gather``   -- gather of rows, positions and scores
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
+* ``tg_kv_gather``        -- lower layers' KV cache gathered to the kept tokens
 * ``tg_chain_create`` / ``TgChain.launch`` -- the four calls captured once as
                           a HIP graph and replayed
 """
@@ -29,7 +30,8 @@ __all__ = [
     "TokenGateError", "lib_path", "load", "kept_count",
     "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
     "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_chain_create", "TgChain",
+    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_kv_gather",
+    "tg_chain_create", "TgChain",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
     "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
 ]
@@ -42,7 +44,8 @@ TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
             "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_chain_create",
+            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_kv_gather",
+            "tg_chain_create",
             "tg_chain_launch", "tg_chain_destroy")
 
 
@@ -69,6 +72,8 @@ class ChainDesc(ctypes.Structure):
         ("Hq", _I64), ("Hkv", _I64), ("D", _I64), ("q", _P), ("k", _P), ("v", _P),
         ("attn_key_score", _P), ("gain", _P), ("q_scale", _P), ("softmax_scale", _F),
         ("causal", _I), ("out", _P), ("lse", _P),
+        ("kv_L", _I64), ("kv_k_cache", _P), ("kv_v_cache", _P), ("kv_k_kept", _P),
+        ("kv_v_kept", _P),
     ]
 
 
@@ -103,6 +108,8 @@ def load():
     lib.tg_compact_gather.restype = I
     lib.tg_bias_attn_fwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P]
     lib.tg_bias_attn_fwd.restype = I
+    lib.tg_kv_gather.argtypes = [I, I64, I64, I64, I64, I64, P, P, P, P, P, P]
+    lib.tg_kv_gather.restype = I
     lib.tg_chain_create.argtypes = [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]
     lib.tg_chain_create.restype = I
     lib.tg_chain_launch.argtypes = [P, P]
@@ -246,6 +253,36 @@ def tg_gate_score_packed(resid, prunable, w1_packed, w2, b2=0.0, b1=None, eps=1e
     return scores
 
 
+def tg_kv_gather(kept_idx, N, k_cache=None, v_cache=None, k_kept=None, v_kept=None,
+                 stream=None):
+    """(k_kept, v_kept) [L, N, Hkv, D] from caches [L, T, Hkv, D] (either may
+    be None); kept_idx is tg_topk_select's output (its first N entries)."""
+    lib = load()
+    ref = k_cache if k_cache is not None else v_cache
+    if ref is None:
+        raise ValueError("give k_cache and/or v_cache")
+    _dev(kept_idx, "kept_idx", torch.int32)
+    L, T, Hkv, D = ref.shape
+    outs = []
+    for c, o, name in ((k_cache, k_kept, "k"), (v_cache, v_kept, "v")):
+        if c is None:
+            outs.append(None)
+            continue
+        _dev(c, name + "_cache", ref.dtype)
+        if tuple(c.shape) != (L, T, Hkv, D) or not c.is_contiguous():
+            raise ValueError(name + "_cache must be a contiguous [L, T, Hkv, D] tensor")
+        if o is None:
+            o = torch.empty((L, int(N), Hkv, D), dtype=c.dtype, device=c.device)
+        _dev(o, name + "_kept", c.dtype)
+        if tuple(o.shape) != (L, int(N), Hkv, D) or not o.is_contiguous():
+            raise ValueError(name + "_kept must be a contiguous [L, N, Hkv, D] tensor")
+        outs.append(o)
+    st = lib.tg_kv_gather(_dt(ref), L, T, int(N), Hkv, D, _ptr(k_cache), _ptr(v_cache),
+                          _ptr(kept_idx), _ptr(outs[0]), _ptr(outs[1]), _stream(stream))
+    _check(st, "tg_kv_gather")
+    return outs[0], outs[1]
+
+
 class TgChain:
     """A captured chain (tg_chain_create); keeps its tensors alive."""
 
@@ -273,7 +310,8 @@ class TgChain:
 def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, workspace,
                     N, resid_kept, pos_kept, score_kept, q, k, v, attn_key_score, gain,
                     out, w1_packed=False, b2=0.0, rms_weight=None, b1=None, eps=1e-6,
-                    q_scale=None, softmax_scale=0.0, causal=True, lse=None):
+                    q_scale=None, softmax_scale=0.0, causal=True, lse=None,
+                    kv_k_cache=None, kv_v_cache=None, kv_k_kept=None, kv_v_kept=None):
     """Capture gate -> top-K -> gather -> bias attention into one HIP graph.
     Every argument is the tensor the corresponding call would take; the graph
     keeps their addresses, so refill inputs in place between launches."""
@@ -291,12 +329,16 @@ def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, wor
         pos_kept=_addr(pos_kept), score_kept=_addr(score_kept), Hq=Hq, Hkv=k.shape[1], D=D,
         q=_addr(q), k=_addr(k), v=_addr(v), attn_key_score=_addr(attn_key_score), gain=_addr(gain),
         q_scale=_addr(q_scale), softmax_scale=float(softmax_scale), causal=1 if causal else 0,
-        out=_addr(out), lse=_addr(lse))
+        out=_addr(out), lse=_addr(lse),
+        kv_L=(kv_k_cache if kv_k_cache is not None else kv_v_cache).shape[0]
+        if (kv_k_cache is not None or kv_v_cache is not None) else 0,
+        kv_k_cache=_addr(kv_k_cache), kv_v_cache=_addr(kv_v_cache),
+        kv_k_kept=_addr(kv_k_kept), kv_v_kept=_addr(kv_v_kept))
     h_out = ctypes.c_void_p()
     _check(lib.tg_chain_create(ctypes.byref(desc), ctypes.byref(h_out)), "tg_chain_create")
     keep = [resid, prunable, w1, w2, scores, kept_idx, n_kept, workspace, resid_kept,
             pos_kept, score_kept, q, k, v, attn_key_score, gain, out, rms_weight, b1,
-            q_scale, lse]
+            q_scale, lse, kv_k_cache, kv_v_cache, kv_k_kept, kv_v_kept]
     return TgChain(h_out, keep)
 
 

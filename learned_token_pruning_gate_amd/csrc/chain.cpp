@@ -14,7 +14,10 @@ struct tg_chain {
 
 namespace {
 
-tg_status run_chain(const tg_chain_desc& d, hipStream_t s) {
+// The optional KV gather forks onto `side` after the residual gather and
+// joins `s` after the attention; fork/join are event edges of the capture.
+tg_status run_chain(const tg_chain_desc& d, hipStream_t s, hipStream_t side, hipEvent_t fork,
+                    hipEvent_t join) {
   tg_status st =
       d.w1_packed
           ? tg_gate_score_packed(d.dt, d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
@@ -29,8 +32,20 @@ tg_status run_chain(const tg_chain_desc& d, hipStream_t s) {
                          d.kept_idx, d.resid_kept, d.kept_row_stride, d.pos_kept, d.score_kept,
                          s);
   if (st != TG_OK) return st;
-  return tg_bias_attn_fwd(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score, d.gain,
-                          d.q_scale, d.softmax_scale, d.causal, d.out, d.lse, s);
+  const bool kv = d.kv_L > 0;
+  if (kv) {
+    if (hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
+      return tg::fail(TG_ERR_LAUNCH, "tg_chain_create: could not fork the KV gather");
+    st = tg_kv_gather(d.dt, d.kv_L, d.T, d.N, d.Hkv, d.D, d.kv_k_cache, d.kv_v_cache, d.kept_idx,
+                      d.kv_k_kept, d.kv_v_kept, side);
+    if (st != TG_OK) return st;
+  }
+  st = tg_bias_attn_fwd(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score, d.gain,
+                        d.q_scale, d.softmax_scale, d.causal, d.out, d.lse, s);
+  if (st != TG_OK) return st;
+  if (kv && (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess))
+    return tg::fail(TG_ERR_LAUNCH, "tg_chain_create: could not join the KV gather");
+  return TG_OK;
 }
 
 }  // namespace
@@ -40,20 +55,35 @@ extern "C" tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain
   if (chain == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "tg_chain_create: chain is NULL");
   *chain = nullptr;
   if (desc == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "tg_chain_create: desc is NULL");
-  hipStream_t cs = nullptr;
+  hipStream_t cs = nullptr, side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  auto release = [&]() {
+    if (side) (void)hipStreamDestroy(side);
+    if (cs) (void)hipStreamDestroy(cs);
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+  };
   hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
-  if (e != hipSuccess)
-    return fail(TG_ERR_LAUNCH, "tg_chain_create: stream creation failed: %s", hipGetErrorString(e));
+  if (e == hipSuccess && desc->kv_L > 0) {
+    e = hipStreamCreateWithFlags(&side, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+  }
+  if (e != hipSuccess) {
+    release();
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: stream/event creation failed: %s",
+                hipGetErrorString(e));
+  }
   e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
   if (e != hipSuccess) {
-    (void)hipStreamDestroy(cs);
+    release();
     return fail(TG_ERR_LAUNCH, "tg_chain_create: capture failed to begin: %s",
                 hipGetErrorString(e));
   }
-  const tg_status st = run_chain(*desc, cs);
+  const tg_status st = run_chain(*desc, cs, side, fork, join);
   hipGraph_t graph = nullptr;
   e = hipStreamEndCapture(cs, &graph);
-  (void)hipStreamDestroy(cs);
+  release();
   if (st != TG_OK) {   // the failing call's message is kept
     if (graph) (void)hipGraphDestroy(graph);
     return st;

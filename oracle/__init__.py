@@ -61,6 +61,8 @@ def _bind(path):
     lib.tgo_topk_select.restype = I64
     lib.tgo_compact_gather.argtypes = [I64, I64, P, I64, P, P, P, P, P]
     lib.tgo_compact_gather.restype = None
+    lib.tgo_kv_gather.argtypes = [I64, I64, I64, I64, P, P, P]
+    lib.tgo_kv_gather.restype = None
     lib.tgo_bias_attn.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, D,
                                   ctypes.c_int, P, I64, P, P]
     lib.tgo_bias_attn.restype = None
@@ -143,6 +145,19 @@ class Oracle:
                                      _ptr(pos), _ptr(sk))
         return out, pos, sk
 
+    def kv_gather(self, cache, kept_idx):
+        """cache [L, T, ...] -> [L, N, ...]: byte-exact gather of token rows."""
+        cache = np.ascontiguousarray(cache)
+        kept_idx = np.ascontiguousarray(kept_idx, dtype=np.int32)
+        L, T = cache.shape[:2]
+        N = kept_idx.shape[0]
+        if N and (kept_idx.min() < 0 or kept_idx.max() >= T):
+            raise IndexError("kept index out of range")
+        row_bytes = cache.strides[1]
+        out = np.empty((L, N) + cache.shape[2:], dtype=cache.dtype)
+        self._lib.tgo_kv_gather(L, T, N, row_bytes, _ptr(cache), _ptr(kept_idx), _ptr(out))
+        return out
+
     def bias_attn(self, q, k, v, key_score, gain, q_scale=None, scale=None,
                   causal=True, rows=None):
         """(out, lse): out [n_rows, Hq, D] fp64, lse [Hq, n_rows] fp64.
@@ -199,6 +214,10 @@ def topk_select(*args, **kwargs):
 
 def compact_gather(*args, **kwargs):
     return default().compact_gather(*args, **kwargs)
+
+
+def kv_gather(*args, **kwargs):
+    return default().kv_gather(*args, **kwargs)
 
 
 def bias_attn(*args, **kwargs):

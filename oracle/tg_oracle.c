@@ -146,6 +146,19 @@ void tgo_compact_gather(int64_t N, int64_t row_bytes, const uint8_t* resid,
 }
 
 /* ---------------------------------------------------------------------- */
+/* Lower layers' KV cache gathered to the kept tokens: for every layer l and */
+/* kept rank r, row (l, r) of the output is row (l, kept_idx[r]) of the     */
+/* cache, byte for byte.                                                    */
+/* ---------------------------------------------------------------------- */
+void tgo_kv_gather(int64_t L, int64_t T, int64_t N, int64_t row_bytes,
+                   const uint8_t* cache, const int32_t* kept_idx, uint8_t* out) {
+  for (int64_t l = 0; l < L; ++l)
+    for (int64_t r = 0; r < N; ++r)
+      memcpy(out + (l * N + r) * row_bytes,
+             cache + (l * T + (int64_t)kept_idx[r]) * row_bytes, (size_t)row_bytes);
+}
+
+/* ---------------------------------------------------------------------- */
 /* Token-gated attention, one (query row, query head) at a time.            */
 /* ---------------------------------------------------------------------- */
 void tgo_bias_attn(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,

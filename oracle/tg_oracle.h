@@ -57,6 +57,14 @@ void tgo_compact_gather(int64_t N, int64_t row_bytes, const uint8_t* resid,
                         const int32_t* kept_idx, uint8_t* resid_kept,
                         int32_t* pos_kept, float* score_kept);
 
+/* Lower layers' KV cache gathered to the kept tokens ([S1] Key
+ * Contributions item 1: upper layers hold no KV entries for pruned tokens;
+ * the lower layers' entries are compacted with the same kept indices):
+ * out[l][r] = cache[l][kept_idx[r]] for l < L, r < N; rows of row_bytes
+ * bytes, cache [L][T] rows, out [L][N] rows. */
+void tgo_kv_gather(int64_t L, int64_t T, int64_t N, int64_t row_bytes,
+                   const uint8_t* cache, const int32_t* kept_idx, uint8_t* out);
+
 /* Token-gated attention forward, [S1] Key Contributions item 2 and 3,
  * Methodology ("added before the online softmax"), [S2] how the gate works:
  * for query row r, query head hq, key c (c <= r when causal):

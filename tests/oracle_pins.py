@@ -323,6 +323,18 @@ def pin_gather_fancy_indexing(orc):
     assert rk.shape == (0, d) and pos.shape == (0,) and sk.shape == (0,)
 
 
+def pin_kv_gather_take(orc):
+    """numpy.take along the token axis (a library routine), bit for bit."""
+    rng = np.random.default_rng(16)
+    for L, T, N in [(1, 9, 4), (3, 131, 40), (2, 64, 64)]:
+        cache = rng.integers(0, 65535, size=(L, T, 2, 8)).astype(np.uint16)
+        idx = np.sort(rng.choice(T, size=N, replace=False)).astype(np.int32)
+        got = orc.kv_gather(cache, idx)
+        assert got.shape == (L, N, 2, 8)
+        assert got.tobytes() == np.take(cache, idx, axis=1).tobytes()
+    assert orc.kv_gather(cache, np.zeros(0, np.int32)).shape == (2, 0, 2, 8)
+
+
 # ===========================================================================
 # Token-gated attention
 # ===========================================================================

@@ -230,3 +230,18 @@ def test_chain_desc_layout_matches_header():
         names.append(first)
         names.extend(p.strip() for p in parts[1:])
     assert [f[0] for f in tg.ChainDesc._fields_] == names
+
+
+def test_kv_gather_validation(lib):
+    def kv(dt=BF16, L=2, T=100, N=10, Hkv=8, D=128, kc=FAKE, vc=FAKE, idx=FAKE, ko=FAKE, vo=FAKE):
+        return lib.tg_kv_gather(dt, L, T, N, Hkv, D, kc, vc, idx, ko, vo, None)
+    assert kv(dt=9) == INVAL
+    assert kv(L=-1) == INVAL
+    assert kv(N=-1) == INVAL
+    assert kv(Hkv=0) == INVAL
+    assert kv(Hkv=1, D=3) == UNSUP     # a row of 3 * 2 bytes is not a multiple of 16
+    assert kv(L=0) == OK and kv(N=0) == OK
+    assert kv(idx=None) == INVAL
+    assert kv(kc=None) == INVAL        # cache and output must come together
+    assert kv(kc=None, ko=None, vc=None, vo=None) == OK   # nothing to gather, nothing launched
+    assert kv(ko=FAKE_ODD) == INVAL

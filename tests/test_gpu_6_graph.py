@@ -15,7 +15,7 @@ from gpu_util import report, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def make_case(w, packed):
+def make_case(w, packed, kv_layers=0):
     g, a = workloads.generate(w)
     dt = w.dtype
     c = dict(resid=to_dev(g.resid, dt), prunable=to_dev(g.prunable), w2=to_dev(g.w2),
@@ -33,10 +33,22 @@ def make_case(w, packed):
              score_kept=torch.empty(N, dtype=torch.float32, device=dev),
              out=torch.empty_like(c["q"]),
              lse=torch.empty((w.Hq, N), dtype=torch.float32, device=dev))
+    if kv_layers:
+        gen = torch.Generator(device=dev).manual_seed(21)
+        for n in ("kv_k_cache", "kv_v_cache"):
+            c[n] = torch.randn((kv_layers, w.T, w.Hkv, w.D), generator=gen, device=dev).to(
+                c["q"].dtype)
+        c["kv_k_kept"] = torch.empty((kv_layers, N, w.Hkv, w.D), dtype=c["q"].dtype, device=dev)
+        c["kv_v_kept"] = torch.empty_like(c["kv_k_kept"])
     return c
 
 
-OUTS = ("scores", "kept_idx", "n_kept", "resid_kept", "pos_kept", "score_kept", "out", "lse")
+OUTS = ("scores", "kept_idx", "n_kept", "resid_kept", "pos_kept", "score_kept", "out", "lse",
+        "kv_k_kept", "kv_v_kept")
+
+
+def outs(c):
+    return [n for n in OUTS if n in c]
 
 
 def eager(c, w, packed):
@@ -51,14 +63,17 @@ def eager(c, w, packed):
     tg.tg_compact_gather(c["resid"], c["scores"], c["kept_idx"], w.n_kept,
                          resid_kept=c["resid_kept"], pos_kept=c["pos_kept"],
                          score_kept=c["score_kept"])
+    if "kv_k_cache" in c:
+        tg.tg_kv_gather(c["kept_idx"], w.n_kept, c["kv_k_cache"], c["kv_v_cache"],
+                        c["kv_k_kept"], c["kv_v_kept"])
     tg.tg_bias_attn_fwd(c["q"], c["k"], c["v"], c["score_kept"], c["gain"], out=c["out"],
                         lse=c["lse"])
     torch.cuda.synchronize()
-    return {n: c[n].clone() for n in OUTS}
+    return {n: c[n].clone() for n in outs(c)}
 
 
 def clobber(c):
-    for n in OUTS:
+    for n in outs(c):
         if c[n].dtype in (torch.float32, torch.bfloat16):
             c[n].fill_(float("nan"))
         else:
@@ -66,7 +81,7 @@ def clobber(c):
 
 
 def same(c, ref, what):
-    for n in OUTS:
+    for n in outs(c):
         a, b = c[n], ref[n]
         if n == "kept_idx":   # entries past the kept count are unspecified
             k = int(ref["n_kept"].item())
@@ -76,28 +91,30 @@ def same(c, ref, what):
 
 
 CASES = [
-    ("tiny", False),
-    ("t16k", True),
-    ("t16k", False),
-    ("multi", True),   # T > 32768: the multi-workgroup top-K and its workspace
+    ("tiny", False, 0),
+    ("t16k", True, 0),
+    ("t16k", False, 0),
+    ("t16k", True, 2),    # with the lower layers' KV gather on a forked stream
+    ("multi", True, 0),   # T > 32768: the multi-workgroup top-K and its workspace
 ]
 
 
-@pytest.mark.parametrize("name,packed", CASES)
-def test_graph_replays_match_eager(name, packed):
+@pytest.mark.parametrize("name,packed,kv_layers", CASES)
+def test_graph_replays_match_eager(name, packed, kv_layers):
     if name == "multi":
         w = replace(workloads.get("t16k"), name="graph-40k", seed=11, T=40000, d=512, h=128,
                     p_lo=100, p_hi=39900, K=700)
     else:
         w = workloads.get(name)
-    c = make_case(w, packed)
+    c = make_case(w, packed, kv_layers)
     ref = eager(c, w, packed)
+    kv = {n: c[n] for n in ("kv_k_cache", "kv_v_cache", "kv_k_kept", "kv_v_kept") if n in c}
     chain = tg.tg_chain_create(
         resid=c["resid"], prunable=c["prunable"], w1=c["w1"], w2=c["w2"], b1=c["b1"],
         eps=w.eps, w1_packed=packed, scores=c["scores"], K=w.K, kept_idx=c["kept_idx"],
         n_kept=c["n_kept"], workspace=c["workspace"], N=w.n_kept, resid_kept=c["resid_kept"],
         pos_kept=c["pos_kept"], score_kept=c["score_kept"], q=c["q"], k=c["k"], v=c["v"],
-        attn_key_score=c["score_kept"], gain=c["gain"], out=c["out"], lse=c["lse"])
+        attn_key_score=c["score_kept"], gain=c["gain"], out=c["out"], lse=c["lse"], **kv)
     for rep in range(3):
         clobber(c)                     # eager work between replays
         torch.cuda.synchronize()
@@ -117,4 +134,4 @@ def test_graph_replays_match_eager(name, packed):
     torch.cuda.synchronize()
     same(c, ref2, name + " refilled")
     chain.close()
-    report("graph_chain_" + name, packed=packed, replays=5, bit_exact=True)
+    report("graph_chain_" + name, packed=packed, kv_layers=kv_layers, replays=5, bit_exact=True)

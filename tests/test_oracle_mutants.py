@@ -41,6 +41,10 @@ MUTANTS = [
      "const int an = 0, bn = 0;"),
     ("gather_pos_is_rank", "pos_kept[r] = (int32_t)t;", "pos_kept[r] = (int32_t)r;"),
     ("gather_score_by_rank", "score_kept[r] = scores[t];", "score_kept[r] = scores[r];"),
+    ("kv_gather_layer0_only", "cache + (l * T + (int64_t)kept_idx[r]) * row_bytes",
+     "cache + ((int64_t)kept_idx[r]) * row_bytes"),
+    ("kv_gather_by_rank", "cache + (l * T + (int64_t)kept_idx[r]) * row_bytes",
+     "cache + (l * T + r) * row_bytes"),
     ("attn_causal_excludes_diag", "causal ? r + 1 : N", "causal ? r : N"),
     ("attn_bias_sign", "scale * dot + gain[hq] * key_score[c]", "scale * dot - gain[hq] * key_score[c]"),
     ("attn_qscale_dot_only", "z[c] = cr * (scale * dot + gain[hq] * key_score[c]);",
