@@ -211,7 +211,8 @@ tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
  * dt            TG_DTYPE_BF16 (bf16 MFMA, fp32 softmax) or TG_DTYPE_F32.
  * N             kept tokens, 0 <= N <= 2^31 - 1 (N == 0 is a no-op).
  * Hq, Hkv       query / KV heads, Hkv >= 1, Hq % Hkv == 0.
- * D             head dim: 64 or 128.
+ * D             head dim: 64, 128 or 256 (ai.info summary "Main Findings":
+ *               the pages' kernel serves 128 for Qwen3 and 256 for Qwen3.5).
  * q             [N][Hq][D] of dt, contiguous.  k, v: [N][Hkv][D] of dt.
  *               16-byte aligned.
  * key_score     [N] f32 gate scores of the kept tokens, or NULL for no bias

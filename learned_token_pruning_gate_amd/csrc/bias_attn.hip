@@ -98,7 +98,7 @@ __device__ __forceinline__ u32x2 split_bf16_triple(float v) {
 }
 
 template <int D, int HPW, int KS, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
-__global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
+__global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
@@ -110,7 +110,8 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
   constexpr int KRPI = 256 / CPR;           // K rows staged per pass
   constexpr int KI = kBK / KRPI;            // K staging passes
-  constexpr int VT = (kBK / 4) * CPR;       // threads that stage V
+  constexpr int VT = (kBK / 4) * CPR;       // (4 keys x 8 dims) pieces of a V tile
+  constexpr int VPC = (VT + 255) / 256;     // V pieces per staging thread
   // KS key streams: stream kh (waves 4kh .. 4kh+3, threads 256kh ..) takes
   // key tiles kh, kh + KS, kh + 2KS, ... with its own LDS buffers; the
   // streams' partial softmax states are merged at the end
@@ -171,13 +172,14 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
 
   // ---- staging roles ------------------------------------------------------
   const int krow = tid / CPR, kchunk = tid % CPR;          // K: row-major copy
-  const int vkg = tid % (kBK / 4), vdc = tid / (kBK / 4);  // V: 4 keys x 8 dims
+  // V: piece tid + 256 pc is keys 4 vkg .. +3 of dims 8 vdc .. +7, with
+  // vkg = piece % 16 and vdc = piece / 16
   const float inv_scale = 1.0f / scale;
   // A -inf score becomes a bias of -2^21 log2 units (in dot-product units):
   // for any per-query scale >= 0.25 the logit falls below kMaskedLog2 and its
   // weight underflows to exactly 0, as deleting the key would give.
   const float masked_bias = -2097152.0f * inv_scale / kLog2e;
-  u32x4 kreg[KI], vreg[4];
+  u32x4 kreg[KI], vreg[VPC][4];
   float sreg = 0.0f;        // staged raw score (its bias is formed at store time)
   const int bias_key = tid % kBK;
   const float bias_gain = (HAS_BIAS && tid < HPW * kBK) ? gain[hg * HPW + tid / kBK] : 0.0f;
@@ -190,11 +192,16 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
     for (int i = 0; i < KI; ++i)
       kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
           k_rs, static_cast<uint32_t>(k0 + krow + KRPI * i) * kv_row + hoff + 16u * kchunk, 0, 0);
-    if (tid < VT) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        vreg[j] = __builtin_amdgcn_raw_buffer_load_b128(
-            v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
+    for (int pc = 0; pc < VPC; ++pc) {
+      const int piece = tid + 256 * pc;
+      const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
+      if (piece < VT) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          vreg[pc][j] = __builtin_amdgcn_raw_buffer_load_b128(
+              v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
+      }
     }
     if (HAS_BIAS && tid < HPW * kBK)   // keys past N read 0
       sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
@@ -204,19 +211,24 @@ __global__ __launch_bounds__(256 * KS, KS == 1 ? 2 : 1) void attn_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < KI; ++i)
       *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kreg[i];
-    if (tid < VT) {
-      // keys 4 vkg .. 4 vkg + 3 go to the slots the PV k-step reads them from
-      const int vslot = 16 * (vkg >> 2) + 4 * vgroup_slot(vkg & 3);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
-        u32x2 lo, hi;
-        lo[0] = pack_lo(vreg[0][w], vreg[1][w]);
-        lo[1] = pack_lo(vreg[2][w], vreg[3][w]);
-        hi[0] = pack_hi(vreg[0][w], vreg[1][w]);
-        hi[1] = pack_hi(vreg[2][w], vreg[3][w]);
-        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + vslot]) = lo;
-        *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + vslot]) = hi;
+    for (int pc = 0; pc < VPC; ++pc) {
+      const int piece = tid + 256 * pc;
+      const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
+      if (piece < VT) {
+        // keys 4 vkg .. 4 vkg + 3 go to the slots the PV k-step reads them from
+        const int vslot = 16 * (vkg >> 2) + 4 * vgroup_slot(vkg & 3);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
+          u32x2 lo, hi;
+          lo[0] = pack_lo(vreg[pc][0][w], vreg[pc][1][w]);
+          lo[1] = pack_lo(vreg[pc][2][w], vreg[pc][3][w]);
+          hi[0] = pack_hi(vreg[pc][0][w], vreg[pc][1][w]);
+          hi[1] = pack_hi(vreg[pc][2][w], vreg[pc][3][w]);
+          *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + vslot]) = lo;
+          *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + vslot]) = hi;
+        }
       }
     }
     if (HAS_BIAS && tid < HPW * kBK)
@@ -482,10 +494,14 @@ void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
                       const float* ks, const float* gain, const float* qs, float scale_log2,
                       uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
                       int32_t npb, int32_t nhg) {
-  if (static_cast<int64_t>(grid.x) <= kTwoStreamMaxGrid)
-    launch_bf16_attn_ks<D, HPW, CAUSAL, 2>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
-                                           scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
-  else
+  // a head-dim 256 tile pair fills the LDS of a CU: one stream only
+  if constexpr (D <= 128) {
+    if (static_cast<int64_t>(grid.x) <= kTwoStreamMaxGrid) {
+      launch_bf16_attn_ks<D, HPW, CAUSAL, 2>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
+                                             scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+      return;
+    }
+  }
     launch_bf16_attn_ks<D, HPW, CAUSAL, 1>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
                                            scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
 }
@@ -525,8 +541,8 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   if (Hq % Hkv != 0)
     return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: Hq %% Hkv != 0 (%lld, %lld)",
                 (long long)Hq, (long long)Hkv);
-  if (D != 64 && D != 128)
-    return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: head dim must be 64 or 128 (D=%lld)",
+  if (D != 64 && D != 128 && D != 256)
+    return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: head dim must be 64, 128 or 256 (D=%lld)",
                 (long long)D);
   if (N * Hq > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_fwd: N * Hq must fit in int32");
@@ -556,6 +572,11 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
           static_cast<const float*>(q), static_cast<const float*>(k),
           static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
           static_cast<float*>(out), lse, n, hq, hkv);
+    else if (D == 256)
+      attn_f32_kernel<256><<<grid, dim3(128), 0, s>>>(
+          static_cast<const float*>(q), static_cast<const float*>(k),
+          static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
+          static_cast<float*>(out), lse, n, hq, hkv);
     else
       attn_f32_kernel<128><<<grid, dim3(128), 0, s>>>(
           static_cast<const float*>(q), static_cast<const float*>(k),
@@ -573,7 +594,11 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   const bool cz = causal != 0, hb = key_score != nullptr, hs = q_scale != nullptr;
 #define TG_ATTN_DISPATCH(DD, HH) \
   launch_bf16_attn_c<DD, HH>(cz, hb, hs, n, hq, hkv, s, qb, kb, vb, key_score, gain, q_scale, sl2, ob, lse)
-  if (D == 128) {
+  if (D == 256) {
+    if (hpw == 4) TG_ATTN_DISPATCH(256, 4);
+    else if (hpw == 2) TG_ATTN_DISPATCH(256, 2);
+    else TG_ATTN_DISPATCH(256, 1);
+  } else if (D == 128) {
     if (hpw == 4) TG_ATTN_DISPATCH(128, 4);
     else if (hpw == 2) TG_ATTN_DISPATCH(128, 2);
     else TG_ATTN_DISPATCH(128, 1);

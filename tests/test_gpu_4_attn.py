@@ -63,6 +63,8 @@ SHAPES = [  # N, Hq, Hkv, D
     (1, 2, 1, 128), (17, 4, 2, 64), (64, 16, 8, 128), (100, 8, 8, 128),
     (255, 8, 2, 128), (300, 16, 2, 128), (129, 6, 2, 64), (612, 16, 8, 128),
     (1000, 4, 4, 64),
+    # head dim 256 (the pages' second supported head dim)
+    (1, 2, 1, 256), (100, 4, 2, 256), (513, 8, 2, 256), (129, 2, 2, 256), (300, 8, 1, 256),
 ]
 
 
@@ -85,6 +87,16 @@ def test_attn_bf16_optional_inputs(bias, qscale):
     o, lse = gpu(q, k, v, s, g, c, "bf16")
     ro, rl = ref(q, k, v, s, g, c, "bf16")
     assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_opt_b%d_q%d" % (bias, qscale))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_f32_head_dim_256(causal):
+    rng = np.random.default_rng(256 + causal)
+    q, k, v, s, g, c = make(rng, 40, 2, 1, 256, "f32")
+    o, lse = gpu(q, k, v, s, g, c, "f32", causal=causal)
+    ro, rl = ref(q, k, v, s, g, c, "f32", causal=causal)
+    assert_close_f32(as_f64(o), ro, "attn_f32_D256_c%d" % causal)
+    assert_close_f32(lse.cpu().numpy(), rl, "attn_f32_D256_lse_c%d" % causal)
 
 
 def test_attn_custom_scale():

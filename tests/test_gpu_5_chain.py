@@ -19,7 +19,7 @@ from gpu_util import (BF16_ABS, F32_REL, as_f64, assert_close_abs, assert_close_
 pytestmark = pytest.mark.gpu
 
 ALL = ["tiny", "tiny-K32", "t16k", "t32k-K100", "t32k-K500", "t32k-K2000", "t32k-scale",
-       "t128k", "t32k-dense"]
+       "t128k", "t32k-dense", "t16k-d256"]
 
 
 def run_chain(w, g, a, planted=None):

@@ -20,10 +20,13 @@ t32k-K2000  bf16   32768   2048  256  256..32511      2000   16/8     128
 t32k-scale  bf16   32768   2048  256  256..32511      2000   16/8     128
 t128k       bf16   131072  2048  256  256..130815     2000   16/8     128
 t32k-dense  bf16   32768   2048  256  256..32511      32256  16/8     128
+t16k-d256   bf16   16384   2048  256  256..16127      2000   8/2      256
 ==========  =====  ======  ====  ===  ==============  =====  =======  ===
 
 The shapes are those of Qwen3-1.7B (hidden 2048, 16 query / 8 KV heads,
-head dim 128), the model the TokenGate pages evaluate; the lengths mirror
+head dim 128), the model the TokenGate pages evaluate (t16k-d256 keeps
+the 16k prompt and takes the pages' other supported head dim, 256, with
+8 query / 2 KV heads, a shape chosen here); the lengths mirror
 their 16k training length and 32k-128k evaluation tiers; the non-prunable
 prefix and suffix mirror the instruction / question text around the
 prunable document; the budgets mirror the README's K sweep.
@@ -127,6 +130,7 @@ WORKLOADS["t32k-K100"] = replace(_BASE["t32k-K2000"], name="t32k-K100", K=100)
 WORKLOADS["t32k-K500"] = replace(_BASE["t32k-K2000"], name="t32k-K500", K=500)
 WORKLOADS["t32k-scale"] = replace(_BASE["t32k-K2000"], name="t32k-scale",
                                   q_scale_recipe="pos_rank")
+WORKLOADS["t16k-d256"] = replace(_BASE["t16k"], name="t16k-d256", seed=6, Hq=8, Hkv=2, D=256)
 
 
 def get(name: str) -> Workload:
