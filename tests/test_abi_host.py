@@ -175,7 +175,7 @@ def test_attn_validation(lib):
     assert _attn(lib, Hkv=0) == INVAL
     assert _attn(lib, Hq=6, Hkv=4) == INVAL           # Hq % Hkv != 0
     assert _attn(lib, D=96) == UNSUP
-    assert _attn(lib, D=256) == UNSUP
+    assert _attn(lib, D=512) == UNSUP
     assert _attn(lib, N=0) == OK
     assert _attn(lib, q=None) == INVAL
     assert _attn(lib, out=None) == INVAL
