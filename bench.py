@@ -11,7 +11,8 @@ before the timed region; outputs are preallocated.
 By default each timed step is one replay of the four calls captured as a HIP
 graph (tg_chain_create); --mode eager launches them one by one.  Per-stage
 times come from HIP events around each call of an eager run of the same
-steps.
+steps.  The attention gets a split-key workspace (tg_bias_attn_fwd_ws) when
+its shape uses one; --attn-split off runs tg_bias_attn_fwd.
 
 Prints one JSON line: tokens/s for the whole step, per-stage event timings,
 the roofline of the dominant kernel, and the CPU oracle timed on a bounded
@@ -145,6 +146,11 @@ def main():
                          "captured as a HIP graph (tg_chain_create, the pages' serving "
                          "recipe) per step, or the four calls launched one by one; "
                          "the per-stage events always come from an eager run")
+    ap.add_argument("--attn-split", choices=["on", "off"], default="on",
+                    help="give the attention a split-key workspace "
+                         "(tg_bias_attn_fwd_ws: long rows' keys cut into chunks on separate "
+                         "workgroups, then merged) when the shape uses one; off runs "
+                         "tg_bias_attn_fwd")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel that "
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -218,8 +224,12 @@ def main():
                 ws.numel(), sp)
     gat_args = (dtc, w.T, N, w.d, P(resid), resid.stride(0), P(scores), P(kept),
                 P(resid_kept), resid_kept.stride(0), P(pos_kept), P(score_kept), sp)
+    att_ws_bytes = (tg.tg_bias_attn_workspace_size(N, w.Hq, w.Hkv, w.D, True, q.dtype)
+                    if args.attn_split == "on" else 0)
+    att_ws = (torch.empty(att_ws_bytes, dtype=torch.uint8, device=dev) if att_ws_bytes
+              else None)
     att_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), key_ptr, P(gain), P(q_scale),
-                F(0.0), 1, P(out), P(lse), sp)
+                F(0.0), 1, P(out), P(lse), P(att_ws), att_ws_bytes, sp)
 
     def check(st, name):
         if st != 0:
@@ -261,7 +271,7 @@ def main():
             if ev is not None:
                 ev[6].record(side)
             join_ev.record(side)
-        check(lib.tg_bias_attn_fwd(*att_args), "tg_bias_attn_fwd")
+        check(lib.tg_bias_attn_fwd_ws(*att_args), "tg_bias_attn_fwd_ws")
         if ev is not None:
             ev[4].record(stream)
         if kvl > 0:
@@ -302,7 +312,7 @@ def main():
             scores=scores, K=w.K, kept_idx=kept, n_kept=n_kept, workspace=ws, N=N,
             resid_kept=resid_kept, pos_kept=pos_kept, score_kept=score_kept, q=q, k=k, v=v,
             attn_key_score=drawn if drawn is not None else score_kept, gain=gain,
-            q_scale=q_scale, out=out, lse=lse,
+            q_scale=q_scale, out=out, lse=lse, attn_workspace=att_ws,
             **(dict(kv_k_cache=kv_k, kv_v_cache=kv_v, kv_k_kept=kv_ko, kv_v_kept=kv_vo)
                if kvl > 0 else {}))
         for _ in range(max(args.warmup, 1)):
@@ -362,7 +372,7 @@ def main():
                    "n_prunable": w.n_prunable, "K": w.K, "N_kept": N, "Hq": w.Hq,
                    "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
                    "gate_w1": "packed" if use_packed else "row-major",
-                   "kv_layers": kvl,
+                   "kv_layers": kvl, "attn_split": att_ws is not None,
                    "parallelism": "single-gpu"},
         "mode": args.mode,
         "eager_ms_per_step": eager_ms,

@@ -233,6 +233,39 @@ tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
                            float* lse, void* stream);
 
 /* --------------------------------------------------------------------------
+ * tg_bias_attn_fwd with a split of the key range (same operation, ai.info
+ * summary "Key Contributions" items 2 and 3; results equal tg_bias_attn_fwd's
+ * within the bf16 tolerance, rounding order aside).  On a bf16 prompt too
+ * short for its workgroups to fill the chip, the longest causal rows alone
+ * set the time; with a workspace the call cuts every long row's key tiles
+ * into chunks run by separate workgroups, each chunk keeps the online-softmax
+ * state (running max, sum, unnormalised output) of its keys, and a second
+ * kernel combines the chunks of each row exactly as the online softmax
+ * combines key tiles.
+ *
+ * tg_bias_attn_workspace_size  bytes the split needs for this shape, or 0
+ *           when the shape runs unsplit (fp32, head dim 256, a grid that
+ *           fills the chip, or rows too short to cut).  Depends only on the
+ *           arguments; invalid arguments also give 0.
+ * workspace device memory of at least that many bytes, 16-byte aligned, or
+ *           NULL: the call then runs unsplit, as tg_bias_attn_fwd.  Needs no
+ *           initialisation; left undefined.  Calls sharing a workspace must
+ *           be ordered on one stream.
+ * Errors: those of tg_bias_attn_fwd, and TG_ERR_WORKSPACE when workspace is
+ * given with workspace_bytes below the size query's value.
+ * ------------------------------------------------------------------------ */
+size_t tg_bias_attn_workspace_size(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                                   int64_t D, int causal);
+
+tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                              int64_t D, const void* q, const void* k,
+                              const void* v, const float* key_score,
+                              const float* gain, const float* q_scale,
+                              float softmax_scale, int causal, void* out,
+                              float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* --------------------------------------------------------------------------
  * Lower layers' KV cache gathered to the kept tokens.  Pages: ai.info summary
  * "Key Contributions" item 1 (layers above the gate never create KV entries
  * for pruned tokens) and "Methodology in Plain English" (the layers below
@@ -266,7 +299,8 @@ tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv
  *
  * tg_chain_desc holds the arguments of the four calls, field for field as
  * documented above (w1_packed selects tg_gate_score_packed; attn_key_score
- * is the attention's key_score, normally score_kept; the kv_ fields, if
+ * is the attention's key_score, normally score_kept; attn_workspace, if not
+ * NULL, selects tg_bias_attn_fwd_ws; the kv_ fields, if
  * kv_L > 0, add tg_kv_gather with the desc's T, N, Hkv, D and kept_idx).  tg_chain_create
  * validates them through the calls themselves (a failing call's status and
  * tg_last_error() come back unchanged and nothing is captured), captures the
@@ -329,6 +363,9 @@ typedef struct tg_chain_desc {
   const void* kv_v_cache;
   void* kv_k_kept;
   void* kv_v_kept;
+  /* optional workspace of tg_bias_attn_fwd_ws (NULL: unsplit attention) */
+  void* attn_workspace;
+  size_t attn_workspace_bytes;
 } tg_chain_desc;
 
 tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain);

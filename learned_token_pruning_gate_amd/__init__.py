@@ -15,6 +15,8 @@ Entry points (same names as the C ABI):
 * ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
 * ``tg_compact_gather``   -- gather of rows, positions and scores
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
+* ``tg_bias_attn_workspace_size`` / ``tg_bias_attn_fwd_ws`` -- the same with
+                          long rows' keys split over workgroups (short prompts)
 * ``tg_kv_gather``        -- lower layers' KV cache gathered to the kept tokens
 * ``tg_chain_create`` / ``TgChain.launch`` -- the four calls captured once as
                           a HIP graph and replayed
@@ -30,8 +32,8 @@ __all__ = [
     "TokenGateError", "lib_path", "load", "kept_count",
     "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
     "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_kv_gather",
-    "tg_chain_create", "TgChain",
+    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_bias_attn_workspace_size",
+    "tg_bias_attn_fwd_ws", "tg_kv_gather", "tg_chain_create", "TgChain",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
     "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
 ]
@@ -44,7 +46,8 @@ TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
             "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_kv_gather",
+            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
+            "tg_bias_attn_workspace_size", "tg_bias_attn_fwd_ws", "tg_kv_gather",
             "tg_chain_create",
             "tg_chain_launch", "tg_chain_destroy")
 
@@ -73,7 +76,7 @@ class ChainDesc(ctypes.Structure):
         ("attn_key_score", _P), ("gain", _P), ("q_scale", _P), ("softmax_scale", _F),
         ("causal", _I), ("out", _P), ("lse", _P),
         ("kv_L", _I64), ("kv_k_cache", _P), ("kv_v_cache", _P), ("kv_k_kept", _P),
-        ("kv_v_kept", _P),
+        ("kv_v_kept", _P), ("attn_workspace", _P), ("attn_workspace_bytes", ctypes.c_size_t),
     ]
 
 
@@ -108,6 +111,11 @@ def load():
     lib.tg_compact_gather.restype = I
     lib.tg_bias_attn_fwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P]
     lib.tg_bias_attn_fwd.restype = I
+    lib.tg_bias_attn_workspace_size.argtypes = [I, I64, I64, I64, I64, I]
+    lib.tg_bias_attn_workspace_size.restype = ctypes.c_size_t
+    lib.tg_bias_attn_fwd_ws.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P,
+                                        ctypes.c_size_t, P]
+    lib.tg_bias_attn_fwd_ws.restype = I
     lib.tg_kv_gather.argtypes = [I, I64, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.tg_kv_gather.restype = I
     lib.tg_chain_create.argtypes = [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]
@@ -311,7 +319,8 @@ def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, wor
                     N, resid_kept, pos_kept, score_kept, q, k, v, attn_key_score, gain,
                     out, w1_packed=False, b2=0.0, rms_weight=None, b1=None, eps=1e-6,
                     q_scale=None, softmax_scale=0.0, causal=True, lse=None,
-                    kv_k_cache=None, kv_v_cache=None, kv_k_kept=None, kv_v_kept=None):
+                    kv_k_cache=None, kv_v_cache=None, kv_k_kept=None, kv_v_kept=None,
+                    attn_workspace=None):
     """Capture gate -> top-K -> gather -> bias attention into one HIP graph.
     Every argument is the tensor the corresponding call would take; the graph
     keeps their addresses, so refill inputs in place between launches."""
@@ -333,12 +342,14 @@ def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, wor
         kv_L=(kv_k_cache if kv_k_cache is not None else kv_v_cache).shape[0]
         if (kv_k_cache is not None or kv_v_cache is not None) else 0,
         kv_k_cache=_addr(kv_k_cache), kv_v_cache=_addr(kv_v_cache),
-        kv_k_kept=_addr(kv_k_kept), kv_v_kept=_addr(kv_v_kept))
+        kv_k_kept=_addr(kv_k_kept), kv_v_kept=_addr(kv_v_kept),
+        attn_workspace=_addr(attn_workspace),
+        attn_workspace_bytes=0 if attn_workspace is None else attn_workspace.numel())
     h_out = ctypes.c_void_p()
     _check(lib.tg_chain_create(ctypes.byref(desc), ctypes.byref(h_out)), "tg_chain_create")
     keep = [resid, prunable, w1, w2, scores, kept_idx, n_kept, workspace, resid_kept,
             pos_kept, score_kept, q, k, v, attn_key_score, gain, out, rms_weight, b1,
-            q_scale, lse, kv_k_cache, kv_v_cache, kv_k_kept, kv_v_kept]
+            q_scale, lse, kv_k_cache, kv_v_cache, kv_k_kept, kv_v_kept, attn_workspace]
     return TgChain(h_out, keep)
 
 
@@ -403,9 +414,31 @@ def tg_compact_gather(resid, scores, kept_idx, N, resid_kept=None, pos_kept=None
     return resid_kept, pos_kept, score_kept
 
 
+def tg_bias_attn_workspace_size(N: int, Hq: int, Hkv: int, D: int, causal=True,
+                                dtype=torch.bfloat16) -> int:
+    """Bytes of the split-key workspace for this shape (0: runs unsplit)."""
+    dt = TG_DTYPE_BF16 if dtype == torch.bfloat16 else TG_DTYPE_F32
+    return int(load().tg_bias_attn_workspace_size(dt, int(N), int(Hq), int(Hkv), int(D),
+                                                  1 if causal else 0))
+
+
+def tg_bias_attn_fwd_ws(q, k, v, key_score, gain, workspace, q_scale=None, softmax_scale=0.0,
+                        causal=True, out=None, lse=None, want_lse=True, stream=None):
+    """tg_bias_attn_fwd with a split-key workspace (a uint8 device tensor of
+    tg_bias_attn_workspace_size bytes, or None)."""
+    return _bias_attn(q, k, v, key_score, gain, q_scale, softmax_scale, causal, out, lse,
+                      want_lse, stream, True, workspace)
+
+
 def tg_bias_attn_fwd(q, k, v, key_score, gain, q_scale=None, softmax_scale=0.0, causal=True,
                      out=None, lse=None, want_lse=True, stream=None):
     """(out [N, Hq, D], lse [Hq, N] or None)."""
+    return _bias_attn(q, k, v, key_score, gain, q_scale, softmax_scale, causal, out, lse,
+                      want_lse, stream, False, None)
+
+
+def _bias_attn(q, k, v, key_score, gain, q_scale, softmax_scale, causal, out, lse, want_lse,
+               stream, ws_entry, workspace):
     lib = load()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _dev(t, n, q.dtype)
@@ -424,6 +457,17 @@ def tg_bias_attn_fwd(q, k, v, key_score, gain, q_scale=None, softmax_scale=0.0, 
     if lse is None and want_lse:
         lse = torch.empty((Hq, N), dtype=torch.float32, device=q.device)
     _dev(lse, "lse", torch.float32, allow_none=True)
+    if ws_entry:
+        if workspace is not None:
+            _dev(workspace, "workspace", torch.uint8)
+        st = lib.tg_bias_attn_fwd_ws(_dt(q), N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(key_score), _ptr(gain), _ptr(q_scale),
+                                     float(softmax_scale), 1 if causal else 0, _ptr(out),
+                                     _ptr(lse), _ptr(workspace),
+                                     0 if workspace is None else workspace.numel(),
+                                     _stream(stream))
+        _check(st, "tg_bias_attn_fwd_ws")
+        return out, lse
     st = lib.tg_bias_attn_fwd(_dt(q), N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v),
                               _ptr(key_score), _ptr(gain), _ptr(q_scale),
                               float(softmax_scale), 1 if causal else 0, _ptr(out), _ptr(lse),

@@ -46,6 +46,14 @@
 //     dispatcher spreads over the 8 XCDs -- keep one KV head per XCD L2.
 //
 // f32 path: one thread per (query, head), fp32 online softmax.
+#include <algorithm>
+#include <deque>
+#include <functional>
+#include <mutex>
+#include <queue>
+#include <type_traits>
+#include <vector>
+
 #include "tg_common.hpp"
 
 namespace tg {
@@ -97,13 +105,52 @@ __device__ __forceinline__ u32x2 split_bf16_triple(float v) {
   return u32x2{hi | (mid << 16), lo};
 }
 
-template <int D, int HPW, int KS, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
+// ---- key-chunk split ---------------------------------------------------------
+// When the grid is small, the longest causal rows alone set the time: one
+// workgroup walks every key tile of its row while most CUs have finished.
+// The split cuts row p's key tiles [0, row_tiles(p)) into chunks of C tiles
+// (items), and packs the items into at most one workgroup per resident slot
+// (bins): full chunks get a bin each, the remainders and the short rows are
+// packed several to a bin, largest first.  A bin walks its items one after
+// the other.  An item of a row with more than one chunk writes its
+// unnormalised softmax state (running max, sum, O^T) to the workspace, and
+// attn_merge_kernel combines a row's chunks; the other items write their
+// output directly.  Launching no more workgroups than the chip holds at once
+// matters: workgroups beyond that are handed out in dispatch order as slots
+// free up, late, whatever their size.
+constexpr int kMaxChunks = 8;     // chunks per row
+constexpr size_t kNoSlot = ~static_cast<size_t>(0);
+constexpr int kMaxBins = 512;     // workgroups per query-head group
+constexpr int kMaxItems = 1024;   // items per query-head group
+
+struct SplitArgs {
+  float* part_o;    // [slot][4 waves][D/32][64 lanes][16] f32: O^T accumulators
+  float* part_ml;   // [slot][4 waves][64 lanes][2] f32: running max (log2 units), sum
+  // slot of chunk c of split row p: ((npb - 1 - p) * nchunk + c) * query-head groups + group
+  int32_t ctiles;   // C, key tiles per chunk
+  int32_t nchunk;   // chunks of the longest row
+};
+// The chunk launch's kernel arguments: the split and its bins (about 3 KB).
+struct SplitLaunch {
+  SplitArgs a;
+  uint16_t bin_first[kMaxBins + 1];   // bin b walks items [bin_first[b], bin_first[b + 1])
+  uint16_t items[kMaxItems];          // item: row p << 3 | chunk c
+};
+struct NoSplit {};
+
+__host__ __device__ inline int row_tiles(int p, int PB, int N, bool causal) {
+  const int end = causal ? ((p + 1) * PB < N ? (p + 1) * PB : N) : N;
+  return (end + kBK - 1) / kBK;
+}
+
+template <int D, int HPW, int KS, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE, bool SPLIT>
 __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
-    int32_t n_pblocks, int32_t n_hgroups) {
+    int32_t n_pblocks, int32_t n_hgroups, std::conditional_t<SPLIT, SplitLaunch, NoSplit> sp) {
+  static_assert(!SPLIT || KS == 1, "a split chunk runs one key stream");
   constexpr int PB = 32 * (4 / HPW);        // query positions per workgroup
   constexpr int DK = D / 16;                // k-steps of S^T = K Q^T (plus one extra)
   constexpr int DB = D / 32;                // 32-row blocks of O^T
@@ -125,15 +172,10 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
   const int hh = lane >> 5;                 // which half of the wave
 
   const int hg = blockIdx.x % n_hgroups;
-  const int prank = blockIdx.x / n_hgroups;
-  const int pblock = CAUSAL ? n_pblocks - 1 - prank : prank;
   const int G = Hq / Hkv;
   const int hw = wave % HPW;
   const int head = hg * HPW + hw;
   const int kvh = (hg * HPW) / G;
-  const int pos0 = pblock * PB + 32 * (wave / HPW);
-  const int my_q = pos0 + l32;
-  const bool q_ok = my_q < N;
 
   const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;     // bytes per token
   const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
@@ -143,32 +185,6 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
       const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(v), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
-
-  // y = ac * (<q, k> + bias'_k), with ac = scale * log2(e) * c_r and the
-  // per-key bias'_k = gain * score_k / scale in dot-product units.
-  const float cr = HAS_QSCALE ? (q_ok ? q_scale[my_q] : 1.0f) : 1.0f;
-  const float ac = scale * kLog2e * cr;
-
-  // Q^T as MFMA B operand (exact bf16): lane (query l32, half hh) holds dims
-  // 16 ks + 8 hh .. +7.  k-step DK is the extra one: [1, 1, 1, 0...] in the
-  // hh = 0 half, matched on the key side by [bias'_hi, bias'_mid, bias'_lo,
-  // 0...], so the MFMA adds the gate bias to every logit.
-  bf16x8 qf[DK + 1];
-  {
-    const uint32_t base = static_cast<uint32_t>(my_q) * q_row +
-                          static_cast<uint32_t>(head) * D * 2 + 16u * hh;
-#pragma unroll
-    for (int ks = 0; ks < DK; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8,
-                                  __builtin_amdgcn_raw_buffer_load_b128(q_rs, base + 32u * ks, 0, 0));
-  }
-  qf[DK] = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
-                                              : u32x4{0, 0, 0, 0});
-  float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
-
-  const int wg_end = CAUSAL ? min((pblock + 1) * PB, N) : N;
-  const int n_tiles = (wg_end + kBK - 1) / kBK;
-  const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
 
   // ---- staging roles ------------------------------------------------------
   const int krow = tid / CPR, kchunk = tid % CPR;          // K: row-major copy
@@ -236,6 +252,37 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
           sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale);
   };
 
+  // One item: query block pblock against key tiles [t_first, t_end) of its
+  // n_tiles; the final output, or (slot != kNoSlot) the unnormalised state.
+  auto run_item = [&](const int pblock, const int t_first, const int t_end, const int n_tiles,
+                      const size_t slot) {
+  const int pos0 = pblock * PB + 32 * (wave / HPW);
+  const int my_q = pos0 + l32;
+  const bool q_ok = my_q < N;
+
+  // y = ac * (<q, k> + bias'_k), with ac = scale * log2(e) * c_r and the
+  // per-key bias'_k = gain * score_k / scale in dot-product units.
+  const float cr = HAS_QSCALE ? (q_ok ? q_scale[my_q] : 1.0f) : 1.0f;
+  const float ac = scale * kLog2e * cr;
+
+  // Q^T as MFMA B operand (exact bf16): lane (query l32, half hh) holds dims
+  // 16 ks + 8 hh .. +7.  k-step DK is the extra one: [1, 1, 1, 0...] in the
+  // hh = 0 half, matched on the key side by [bias'_hi, bias'_mid, bias'_lo,
+  // 0...], so the MFMA adds the gate bias to every logit.
+  bf16x8 qf[DK + 1];
+  {
+    const uint32_t base = static_cast<uint32_t>(my_q) * q_row +
+                          static_cast<uint32_t>(head) * D * 2 + 16u * hh;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8,
+                                  __builtin_amdgcn_raw_buffer_load_b128(q_rs, base + 32u * ks, 0, 0));
+  }
+  qf[DK] = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
+                                              : u32x4{0, 0, 0, 0});
+  float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
+  const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
+
   // ---- running state --------------------------------------------------------
   f32x16 o[DB];
 #pragma unroll
@@ -244,22 +291,22 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
     for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
   float l_run = 0.0f;       // this lane's share of the running sum of 2^y
 
-  if (kh < n_tiles) {
-    load_tile(kh);
+  if (t_first + kh < t_end) {
+    load_tile(t_first + kh);
     store_tile(sm[0][kh]);
   }
   __syncthreads();
 
-  const int n_rounds = (n_tiles + KS - 1) / KS;
+  const int n_rounds = (t_end - t_first + KS - 1) / KS;
   for (int j = 0; j < n_rounds; ++j) {
-    const int t = KS * j + kh;               // this stream's tile
+    const int t = t_first + KS * j + kh;     // this stream's tile
     const AttnSmem<D>& b = sm[j & 1][kh];
     const int k0 = t * kBK;
-    const bool more = t + KS < n_tiles;
+    const bool more = t + KS < t_end;
     if (more) load_tile(t + KS);
     // keep the next tile's loads issued here, ahead of this tile's math
     __builtin_amdgcn_sched_barrier(0);
-    if (KS == 1 || t < n_tiles) {   // uniform per wave: a stream may idle in the last round
+    if (KS == 1 || t < t_end) {   // uniform per wave: a stream may idle in the last round
 
     // S'^T = K' Q'^T = <q, k> + bias'; the two 32-key halves are independent
     // accumulation chains, interleaved so neither waits on its own last MFMA
@@ -393,6 +440,21 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
 
   // ---- epilogue -------------------------------------------------------------
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  if constexpr (SPLIT) {
+    if (slot != kNoSlot) {
+      // one chunk of a split row: hand the unnormalised state to the merge
+      const size_t ws = slot * 4 + wave;
+      float* po = sp.a.part_o + (ws * DB * 64 + lane) * 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<f32x4*>(po + db * 64 * 16 + 4 * j) =
+              f32x4{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
+      *reinterpret_cast<float2*>(sp.a.part_ml + ws * 128 + 2 * lane) = make_float2(m_run, l_tot);
+      return;
+    }
+  }
   const bool empty = !(l_tot > 0.0f) || m_run == -INFINITY;  // no visible key
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (q_ok) {
@@ -411,6 +473,105 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
       lse[static_cast<int64_t>(head) * N + my_q] =
           empty ? -INFINITY : kLn2 * (m_run + __builtin_log2f(l_tot));
   }
+  };
+
+  if constexpr (SPLIT) {
+    const int bin = blockIdx.x / n_hgroups;
+    const int i_end = sp.bin_first[bin + 1];
+    for (int i = sp.bin_first[bin]; i < i_end; ++i) {
+      const int item = sp.items[i];
+      const int p = item >> 3, c = item & 7;
+      const int nt = row_tiles(p, PB, N, CAUSAL);
+      const int t0 = c * sp.a.ctiles;
+      const size_t slot =
+          nt > sp.a.ctiles
+              ? (static_cast<size_t>(n_pblocks - 1 - p) * sp.a.nchunk + c) * n_hgroups + hg
+              : kNoSlot;
+      run_item(p, t0, min(t0 + sp.a.ctiles, nt), nt, slot);
+    }
+  } else {
+    const int prank = blockIdx.x / n_hgroups;
+    const int pblock = CAUSAL ? n_pblocks - 1 - prank : prank;
+    const int nt = row_tiles(pblock, PB, N, CAUSAL);
+    run_item(pblock, 0, nt, nt, kNoSlot);
+  }
+}
+
+// Combines the chunks of every split row: with the chunks' running maxima
+// m_c (log2 units), sums l_c and unnormalised O_c,
+//   M = max_c m_c,  w_c = 2^(m_c - M),  O = sum_c w_c O_c / sum_c w_c l_c,
+// the state one pass over all keys reaches.  One workgroup per (split row,
+// query-head group, 32-dim block of O); thread (wave, lane) owns the
+// accumulator entries that lane of that wave held in the chunk workgroups.
+template <int D, int HPW, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_merge_kernel(SplitArgs sp, uint16_t* __restrict__ out,
+                                                         float* __restrict__ lse, int32_t N,
+                                                         int32_t Hq, int32_t n_pblocks,
+                                                         int32_t n_hgroups) {
+  constexpr int PB = 32 * (4 / HPW);
+  constexpr int DB = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  // the query-head group is the fastest index, as in the chunk launch, so a
+  // group's merge runs on the XCD whose L2 holds its chunk states
+  const int hg = blockIdx.x % n_hgroups;
+  const int db = (blockIdx.x / n_hgroups) % DB;
+  const int rank = static_cast<int>(blockIdx.x) / (n_hgroups * DB);   // split rows, longest first
+  const int pblock = n_pblocks - 1 - rank;
+  const int head = hg * HPW + wave % HPW;
+  const int my_q = pblock * PB + 32 * (wave / HPW) + l32;
+  const int nc = (row_tiles(pblock, PB, N, CAUSAL) + sp.ctiles - 1) / sp.ctiles;
+
+  // every load first (one round trip), then the combination
+  float2 ml[kMaxChunks];
+  f32x4 ov[kMaxChunks][4];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c < nc) {
+      const size_t slot = ((static_cast<size_t>(rank) * sp.nchunk + c) * n_hgroups + hg) * 4 + wave;
+      ml[c] = *reinterpret_cast<const float2*>(sp.part_ml + slot * 128 + 2 * lane);
+      const f32x4* po =
+          reinterpret_cast<const f32x4*>(sp.part_o + ((slot * DB + db) * 64 + lane) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ov[c][j] = po[j];
+    }
+  }
+  float m_max = -INFINITY;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    if (c < nc) m_max = fmaxf(m_max, ml[c].x);
+  float l_tot = 0.0f;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    if (c < nc) {
+      const float w = ml[c].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ml[c].x - m_max);
+      l_tot += w * ml[c].y;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(w, ov[c][j][i], acc[j][i]);
+    }
+  }
+  const bool empty = !(l_tot > 0.0f) || m_max == -INFINITY;
+  const float inv = empty ? 0.0f : 1.0f / l_tot;
+  if (my_q >= N) return;
+  uint16_t* op = out + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D +
+                 32 * db + 4 * hh;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    bf16x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = static_cast<__bf16>(acc[j][i] * inv);
+    *reinterpret_cast<bf16x4*>(op + 8 * j) = v;
+  }
+  if (lse != nullptr && hh == 0 && db == 0)
+    lse[static_cast<int64_t>(head) * N + my_q] =
+        empty ? -INFINITY : kLn2 * (m_max + __builtin_log2f(l_tot));
 }
 
 // ---------------------------------------------------------------------------
@@ -470,68 +631,218 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 // cost of a whole CU's LDS per workgroup: they pay off while the grid is too
 // small to keep every CU busy with one-stream workgroups for several rounds.
 constexpr int64_t kTwoStreamMaxGrid = 1024;
+// Workgroups of the one-stream head-dim <= 128 kernel resident at once on
+// the chip (256 CUs, two per CU); two-stream workgroups take a whole CU.
+constexpr int kSlots1 = 512, kSlots2 = 256;
+constexpr int kMinChunkTiles = 4;
+// Cost model, in units of one key tile of one workgroup (~2.4 us at head
+// dim 128 with two workgroups per CU): each item adds its setup (Q and first
+// tile loads) and epilogue; the merge costs a launch plus the chunk states'
+// bytes read back at about 10 MB per unit.
+constexpr double kItemUnits = 1.5;
+// A two-stream workgroup's round of two tiles takes ~1.3 units (its eight
+// waves share every barrier).
+constexpr double kTwoStreamRoundUnits = 1.3;
+constexpr double kMergeFixedUnits = 1.0;
+constexpr double kMergeBytesPerUnit = 10.0e6;
+// The split must beat the unsplit launch by this factor to be used.
+constexpr double kSplitGain = 0.92;
 
-template <int D, int HPW, bool CAUSAL, int KS>
-void launch_bf16_attn_ks(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
-                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const float* ks, const float* gain, const float* qs, float scale_log2,
-                      uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
-                      int32_t npb, int32_t nhg) {
-#define TG_ATTN_LAUNCH(B, Q)                                                         \
-  attn_bf16_kernel<D, HPW, KS, CAUSAL, B, Q><<<grid, dim3(256 * KS), 0, s>>>(        \
-      q, k, v, ks, gain, qs, scale_log2, out, lse, N, Hq, Hkv, npb, nhg)
-  if (has_bias) {
-    if (has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
+struct AttnArgs {
+  const uint16_t *q, *k, *v;
+  const float *ks, *gain, *qs;
+  float scale;
+  uint16_t* out;
+  float* lse;
+  int32_t N, Hq, Hkv;
+  bool causal, has_bias, has_qs;
+  hipStream_t s;
+};
+
+// Key-chunk split of a bf16 launch (ctiles == 0: the launch runs unsplit).
+struct SplitPlan {
+  int32_t ctiles = 0, nchunk = 0, n_bins = 0, n_split_rows = 0;
+  size_t part_o_floats = 0, bytes = 0;
+  std::vector<uint16_t> bin_first, items;
+};
+
+// Greedy list schedule of tasks (sizes in tile units, in dispatch order) on
+// `slots` identical workgroup slots: the time the last one ends.
+double list_schedule(const std::vector<double>& tasks, int slots) {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  for (int i = 0; i < slots; ++i) free_at.push(0.0);
+  double end = 0.0;
+  for (double t : tasks) {
+    const double s = free_at.top();
+    free_at.pop();
+    end = std::max(end, s + t);
+    free_at.push(s + t);
+  }
+  return end;
+}
+
+SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal) {
+  SplitPlan best_plan;
+  if (N <= 0 || D > 128) return best_plan;   // head dim 256 keeps one workgroup per CU
+  const int64_t G = Hq / Hkv;
+  const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  const int PB = 32 * (4 / hpw);
+  const int npb = static_cast<int>((N + PB - 1) / PB), nhg = static_cast<int>(Hq / hpw);
+  if (static_cast<int64_t>(npb) * nhg > kTwoStreamMaxGrid) return best_plan;
+  const int n = static_cast<int>(N);
+  const int nt_max = row_tiles(npb - 1, PB, n, causal);
+  const int max_bins = std::min(kMaxBins, kSlots1 / nhg);
+  if (max_bins < 1) return best_plan;
+  // unsplit: two key streams per workgroup, each walking half of its row
+  std::vector<double> tasks;
+  for (int p = npb - 1; p >= 0; --p)
+    for (int h = 0; h < nhg; ++h)
+      tasks.push_back((row_tiles(p, PB, n, causal) + 1) / 2 * kTwoStreamRoundUnits + kItemUnits);
+  double best = list_schedule(tasks, kSlots2) * kSplitGain;
+  const size_t state_bytes = static_cast<size_t>(4) * ((D / 32) * 16 * 64 + 128) * sizeof(float);
+  struct Item {
+    int size, p, c;
+  };
+  std::vector<Item> full, rest;
+  for (int C = std::max((nt_max + kMaxChunks - 1) / kMaxChunks, kMinChunkTiles); C < nt_max;
+       ++C) {
+    const int nchunk = (nt_max + C - 1) / C;
+    full.clear();
+    rest.clear();
+    int split_rows = 0;
+    int64_t states = 0;   // chunk states written and merged, per query-head group
+    for (int p = npb - 1; p >= 0; --p) {
+      const int nt = row_tiles(p, PB, n, causal);
+      if (nt > C) {
+        ++split_rows;
+        states += (nt + C - 1) / C;
+      }
+      for (int c = 0; c * C < nt; ++c) {
+        const int size = std::min(C, nt - c * C);
+        (size == C ? full : rest).push_back(Item{size, p, c});
+      }
+    }
+    if (full.size() + rest.size() > static_cast<size_t>(kMaxItems)) continue;
+    // full chunks first, then the rest largest first (ties: longer row first)
+    std::stable_sort(rest.begin(), rest.end(),
+                     [](const Item& a, const Item& b) { return a.size > b.size; });
+    std::vector<Item> order(full);
+    order.insert(order.end(), rest.begin(), rest.end());
+    // next-fit packing into the fewest-cost bins that number at most max_bins
+    std::vector<uint16_t> first;
+    double cap = C + kItemUnits, makespan = 0.0;
+    for (;; cap += 0.25) {
+      first.assign(1, 0);
+      double fill = 0.0;
+      makespan = 0.0;
+      for (size_t i = 0; i < order.size(); ++i) {
+        const double cost = order[i].size + kItemUnits;
+        if (fill > 0.0 && fill + cost > cap) {
+          first.push_back(static_cast<uint16_t>(i));
+          fill = 0.0;
+        }
+        fill += cost;
+        makespan = std::max(makespan, fill);
+      }
+      first.push_back(static_cast<uint16_t>(order.size()));
+      if (static_cast<int>(first.size()) - 1 <= max_bins) break;
+    }
+    const double t = makespan + kMergeFixedUnits +
+                     static_cast<double>(states * nhg) * state_bytes / kMergeBytesPerUnit;
+    if (t < best) {
+      best = t;
+      best_plan.ctiles = C;
+      best_plan.nchunk = nchunk;
+      best_plan.n_bins = static_cast<int32_t>(first.size()) - 1;
+      best_plan.n_split_rows = split_rows;
+      best_plan.bin_first = first;
+      best_plan.items.clear();
+      for (const Item& it : order)
+        best_plan.items.push_back(static_cast<uint16_t>((it.p << 3) | it.c));
+    }
+  }
+  if (best_plan.ctiles == 0) return best_plan;
+  const size_t slots = static_cast<size_t>(best_plan.n_split_rows) * best_plan.nchunk * nhg;
+  best_plan.part_o_floats = slots * 4 * (D / 32) * 16 * 64;
+  best_plan.bytes = slots * state_bytes;
+  return best_plan;
+}
+
+// Plans depend only on the shape; the few shapes a process uses are kept.
+const SplitPlan& split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal) {
+  struct Entry {
+    int64_t N, Hq, Hkv, D;
+    bool causal;
+    SplitPlan plan;
+  };
+  static std::mutex mu;
+  static std::deque<Entry> cache;   // entries are never erased: references stay valid
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry& e : cache)
+    if (e.N == N && e.Hq == Hq && e.Hkv == Hkv && e.D == D && e.causal == causal) return e.plan;
+  cache.push_back(Entry{N, Hq, Hkv, D, causal, make_split_plan(N, Hq, Hkv, D, causal)});
+  return cache.back().plan;
+}
+
+template <int D, int HPW, bool CAUSAL, int KS, bool SPLIT, typename SP>
+void launch_bf16_attn_ks(const AttnArgs& a, dim3 grid, int32_t npb, int32_t nhg, const SP& sp) {
+#define TG_ATTN_LAUNCH(B, Q)                                                                  \
+  attn_bf16_kernel<D, HPW, KS, CAUSAL, B, Q, SPLIT><<<grid, dim3(256 * KS), 0, a.s>>>(       \
+      a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.out, a.lse, a.N, a.Hq, a.Hkv, npb, nhg, sp)
+  if (a.has_bias) {
+    if (a.has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
   } else {
-    if (has_qs) TG_ATTN_LAUNCH(false, true); else TG_ATTN_LAUNCH(false, false);
+    if (a.has_qs) TG_ATTN_LAUNCH(false, true); else TG_ATTN_LAUNCH(false, false);
   }
 #undef TG_ATTN_LAUNCH
 }
 
 template <int D, int HPW, bool CAUSAL>
-void launch_bf16_attn(bool has_bias, bool has_qs, dim3 grid, hipStream_t s,
-                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const float* ks, const float* gain, const float* qs, float scale_log2,
-                      uint16_t* out, float* lse, int32_t N, int32_t Hq, int32_t Hkv,
-                      int32_t npb, int32_t nhg) {
-  // a head-dim 256 tile pair fills the LDS of a CU: one stream only
+void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
+  constexpr int PB = 32 * (4 / HPW);
+  const int32_t npb = (a.N + PB - 1) / PB;
+  const int32_t nhg = a.Hq / HPW;
+  const NoSplit none{};
   if constexpr (D <= 128) {
-    if (static_cast<int64_t>(grid.x) <= kTwoStreamMaxGrid) {
-      launch_bf16_attn_ks<D, HPW, CAUSAL, 2>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
-                                             scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+    if (pl.ctiles > 0 && workspace != nullptr) {
+      SplitLaunch sl{};
+      sl.a.part_o = static_cast<float*>(workspace);
+      sl.a.part_ml = sl.a.part_o + pl.part_o_floats;
+      sl.a.ctiles = pl.ctiles;
+      sl.a.nchunk = pl.nchunk;
+      std::copy(pl.bin_first.begin(), pl.bin_first.end(), sl.bin_first);
+      std::copy(pl.items.begin(), pl.items.end(), sl.items);
+      launch_bf16_attn_ks<D, HPW, CAUSAL, 1, true>(
+          a, dim3(static_cast<uint32_t>(pl.n_bins * nhg)), npb, nhg, sl);
+      attn_merge_kernel<D, HPW, CAUSAL>
+          <<<dim3(static_cast<uint32_t>(pl.n_split_rows * (D / 32) * nhg)), dim3(256), 0, a.s>>>(
+              sl.a, a.out, a.lse, a.N, a.Hq, npb, nhg);
       return;
     }
   }
-    launch_bf16_attn_ks<D, HPW, CAUSAL, 1>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
-                                           scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(npb) * nhg));
+  // a head-dim 256 tile pair fills the LDS of a CU: one stream only
+  if constexpr (D <= 128) {
+    if (static_cast<int64_t>(grid.x) <= kTwoStreamMaxGrid) {
+      launch_bf16_attn_ks<D, HPW, CAUSAL, 2, false>(a, grid, npb, nhg, none);
+      return;
+    }
+  }
+  launch_bf16_attn_ks<D, HPW, CAUSAL, 1, false>(a, grid, npb, nhg, none);
 }
 
 template <int D, int HPW>
-void launch_bf16_attn_c(bool causal, bool has_bias, bool has_qs, int32_t N, int32_t Hq,
-                        int32_t Hkv, hipStream_t s, const uint16_t* q, const uint16_t* k,
-                        const uint16_t* v, const float* ks, const float* gain,
-                        const float* qs, float scale_log2, uint16_t* out, float* lse) {
-  constexpr int PB = 32 * (4 / HPW);
-  const int32_t npb = (N + PB - 1) / PB;
-  const int32_t nhg = Hq / HPW;
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(npb) * nhg));
-  if (causal)
-    launch_bf16_attn<D, HPW, true>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
-                                   scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+void launch_bf16_attn_c(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
+  if (a.causal)
+    launch_bf16_attn<D, HPW, true>(a, pl, workspace);
   else
-    launch_bf16_attn<D, HPW, false>(has_bias, has_qs, grid, s, q, k, v, ks, gain, qs,
-                                    scale_log2, out, lse, N, Hq, Hkv, npb, nhg);
+    launch_bf16_attn<D, HPW, false>(a, pl, workspace);
 }
 
-}  // namespace
-}  // namespace tg
-
-extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
-                                      int64_t D, const void* q, const void* k, const void* v,
-                                      const float* key_score, const float* gain,
-                                      const float* q_scale, float softmax_scale, int causal,
-                                      void* out, float* lse, void* stream) {
-  using namespace tg;
+tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, const void* q,
+                   const void* k, const void* v, const float* key_score, const float* gain,
+                   const float* q_scale, float softmax_scale, int causal, void* out,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
     return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: unknown dtype %d", (int)dt);
   if (N < 0 || N > kMaxTokens || Hq < 1 || Hkv < 1 || Hq > 65536 || Hkv > 65536)
@@ -550,6 +861,15 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_bias_attn_fwd: bf16 path addresses Q/K/V with 32-bit offsets "
                 "(N * Hq * D * 2 must be < 2^31)");
+  static const SplitPlan kUnsplit;
+  const SplitPlan& pl = dt == TG_DTYPE_BF16 ? split_plan(N, Hq, Hkv, D, causal != 0) : kUnsplit;
+  if (workspace != nullptr) {
+    if (!aligned(workspace, 16))
+      return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd_ws: workspace must be 16-byte aligned");
+    if (workspace_bytes < pl.bytes)
+      return fail(TG_ERR_WORKSPACE, "tg_bias_attn_fwd_ws: workspace of %zu bytes, need %zu",
+                  workspace_bytes, pl.bytes);
+  }
   if (N == 0) {
     clear_error();
     return TG_OK;
@@ -586,14 +906,11 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   }
   const int64_t G = Hq / Hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const auto* qb = static_cast<const uint16_t*>(q);
-  const auto* kb = static_cast<const uint16_t*>(k);
-  const auto* vb = static_cast<const uint16_t*>(v);
-  auto* ob = static_cast<uint16_t*>(out);
-  const float sl2 = scale;
-  const bool cz = causal != 0, hb = key_score != nullptr, hs = q_scale != nullptr;
-#define TG_ATTN_DISPATCH(DD, HH) \
-  launch_bf16_attn_c<DD, HH>(cz, hb, hs, n, hq, hkv, s, qb, kb, vb, key_score, gain, q_scale, sl2, ob, lse)
+  const AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                   static_cast<const uint16_t*>(v), key_score, gain, q_scale, scale,
+                   static_cast<uint16_t*>(out), lse, n, hq, hkv, causal != 0,
+                   key_score != nullptr, q_scale != nullptr, s};
+#define TG_ATTN_DISPATCH(DD, HH) launch_bf16_attn_c<DD, HH>(a, pl, workspace)
   if (D == 256) {
     if (hpw == 4) TG_ATTN_DISPATCH(256, 4);
     else if (hpw == 2) TG_ATTN_DISPATCH(256, 2);
@@ -609,4 +926,34 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   }
 #undef TG_ATTN_DISPATCH
   return check_launch("tg_bias_attn_fwd");
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                                      int64_t D, const void* q, const void* k, const void* v,
+                                      const float* key_score, const float* gain,
+                                      const float* q_scale, float softmax_scale, int causal,
+                                      void* out, float* lse, void* stream) {
+  return tg::attn_fwd(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale, softmax_scale,
+                      causal, out, lse, nullptr, 0, stream);
+}
+
+extern "C" size_t tg_bias_attn_workspace_size(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                                              int64_t D, int causal) {
+  if (dt != TG_DTYPE_BF16 || N <= 0 || N > tg::kMaxTokens || Hq < 1 || Hkv < 1 ||
+      Hq % Hkv != 0 || (D != 64 && D != 128 && D != 256) || N * Hq * D * 2 > tg::kMaxTokens)
+    return 0;
+  return tg::split_plan(N, Hq, Hkv, D, causal != 0).bytes;
+}
+
+extern "C" tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                                         int64_t D, const void* q, const void* k, const void* v,
+                                         const float* key_score, const float* gain,
+                                         const float* q_scale, float softmax_scale, int causal,
+                                         void* out, float* lse, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  return tg::attn_fwd(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale, softmax_scale,
+                      causal, out, lse, workspace, workspace_bytes, stream);
 }

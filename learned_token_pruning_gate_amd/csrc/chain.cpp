@@ -40,8 +40,9 @@ tg_status run_chain(const tg_chain_desc& d, hipStream_t s, hipStream_t side, hip
                       d.kv_k_kept, d.kv_v_kept, side);
     if (st != TG_OK) return st;
   }
-  st = tg_bias_attn_fwd(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score, d.gain,
-                        d.q_scale, d.softmax_scale, d.causal, d.out, d.lse, s);
+  st = tg_bias_attn_fwd_ws(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score,
+                           d.gain, d.q_scale, d.softmax_scale, d.causal, d.out, d.lse,
+                           d.attn_workspace, d.attn_workspace_bytes, s);
   if (st != TG_OK) return st;
   if (kv && (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess))
     return tg::fail(TG_ERR_LAUNCH, "tg_chain_create: could not join the KV gather");

@@ -184,6 +184,41 @@ def test_attn_validation(lib):
     assert _attn(lib, N=2**30, Hq=4, Hkv=2) == UNSUP  # N * Hq beyond int32
 
 
+def _attn_ws(lib, ws, nbytes, dt=BF16, N=2512, Hq=16, Hkv=8, D=128, q=FAKE, out=FAKE):
+    return lib.tg_bias_attn_fwd_ws(dt, N, Hq, Hkv, D, q, FAKE, FAKE, FAKE, FAKE, None,
+                                   ctypes.c_float(0.0), 1, out, None, ws, nbytes, None)
+
+
+def test_attn_workspace_size(lib):
+    size = lambda *a: lib.tg_bias_attn_workspace_size(*a)
+    # N = 2512, 16/8 heads, D = 128, causal: 40 rows of 64 queries (row p has
+    # p + 1 key tiles) x 8 head groups; the plan cuts rows into chunks of 15
+    # tiles, so rows 15..39 (25 rows) are split, each with state slots for 3
+    # chunks per head group: 25 x 3 x 8 slots of 4 waves x (4 x 16 x 64 + 128)
+    # floats
+    assert size(BF16, 2512, 16, 8, 128, 1) == 25 * 3 * 8 * 4 * (4 * 16 * 64 + 128) * 4
+    assert size(F32, 2512, 16, 8, 128, 1) == 0          # fp32 path never splits
+    assert size(BF16, 2512, 16, 8, 256, 1) == 0         # head dim 256 never splits
+    assert size(BF16, 32768, 16, 8, 128, 1) == 0        # grid fills the chip
+    assert size(BF16, 100, 16, 8, 128, 1) == 0          # rows too short to cut
+    assert size(BF16, 0, 16, 8, 128, 1) == 0
+    assert size(BF16, 2512, 6, 4, 128, 1) == 0          # invalid: Hq % Hkv != 0
+    assert size(BF16, 2512, 16, 8, 96, 1) == 0          # invalid head dim
+    assert size(BF16, 2512, 16, 8, 128, 0) > 0          # non-causal rows split too
+
+
+def test_attn_ws_validation(lib):
+    need = lib.tg_bias_attn_workspace_size(BF16, 2512, 16, 8, 128, 1)
+    assert _attn_ws(lib, FAKE, 0) == WS
+    assert b"workspace" in lib.tg_last_error()
+    assert _attn_ws(lib, FAKE, need - 1) == WS
+    assert _attn_ws(lib, FAKE_ODD, need) == INVAL
+    assert _attn_ws(lib, FAKE, need, q=None) == INVAL
+    assert _attn_ws(lib, None, 0, q=None) == INVAL      # NULL workspace: unsplit checks
+    assert _attn_ws(lib, FAKE, need, D=96) == UNSUP
+    assert _attn_ws(lib, FAKE, 0, N=0) == OK            # nothing to do, nothing needed
+
+
 def test_product_binding_refuses_cpu_tensors():
     import torch
     import learned_token_pruning_gate_amd as tg

@@ -35,6 +35,21 @@ def gpu(q, k, v, s, g, c, dtype, causal=True, scale=0.0):
     return o, lse
 
 
+def gpu_split(q, k, v, s, g, c, causal=True):
+    """The split-key entry point with a workspace of the queried size (the
+    shape must be one that splits)."""
+    N, Hq, D = q.shape
+    nb = tg.tg_bias_attn_workspace_size(N, Hq, k.shape[1], D, causal)
+    assert nb > 0, "shape runs unsplit"
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xFF)   # the call needs no initialised workspace (0xFF.. floats are NaN)
+    o, lse = tg.tg_bias_attn_fwd_ws(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                    None if s is None else to_dev(s), to_dev(g), ws,
+                                    None if c is None else to_dev(c), causal=causal)
+    torch.cuda.synchronize()
+    return o, lse
+
+
 def ref(q, k, v, s, g, c, dtype, causal=True, rows=None):
     N = q.shape[0]
     ss = np.zeros(N) if s is None else s
@@ -197,3 +212,89 @@ def test_attn_bf16_dense_sampled_rows():
     ro, rl = ref(a.q, a.k, a.v, a.drawn_scores, a.gain, c, "bf16", rows=rows)
     assert_close_abs(as_f64(o)[rows], ro, BF16_ABS, "attn_bf16_dense_sampled")
     assert_close_abs(lse.cpu().numpy()[:, rows], rl, LSE_ABS_BF16, "attn_bf16_dense_lse")
+
+
+# ---- split-key path (tg_bias_attn_fwd_ws) ---------------------------------------
+SPLIT_SHAPES = [  # N, Hq, Hkv, D, causal: each takes the split (3 to 7 chunks per long row)
+    (1000, 16, 2, 128, True), (1000, 16, 2, 128, False),   # 4 heads per KV head
+    (1000, 4, 4, 64, True), (1000, 4, 4, 64, False),       # 1 head per KV head
+    (1700, 6, 2, 64, True), (1700, 6, 2, 64, False),       # 3 heads per KV head
+    (2512, 16, 8, 128, True), (2512, 16, 8, 128, False),   # the 16k prompt's kept set
+    (1500, 16, 8, 128, True),
+    (1800, 12, 4, 64, True),
+    (2999, 8, 8, 128, True),                               # ragged last query block
+    (4000, 8, 8, 128, True),
+    (2000, 16, 8, 64, True),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D,causal", SPLIT_SHAPES)
+def test_attn_bf16_split_shapes(N, Hq, Hkv, D, causal):
+    rng = np.random.default_rng(N * 37 + Hq + D + causal)
+    q, k, v, s, g, c = make(rng, N, Hq, Hkv, D, "bf16")
+    o, lse = gpu_split(q, k, v, s, g, c, causal=causal)
+    ro, rl = ref(q, k, v, s, g, c, "bf16", causal=causal)
+    tag = "attn_split_N%d_H%d_%d_D%d_c%d" % (N, Hq, Hkv, D, causal)
+    assert_close_abs(as_f64(o), ro, BF16_ABS, tag)
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, tag + "_lse")
+
+
+def test_attn_split_masked_chunks():
+    """Keys 0..1599 deleted by a -inf score: for the long rows, whole chunks
+    hold no visible key (running max -inf, sum 0) and the merge must skip
+    them; rows 0..1599 see no key at all (O = 0, lse = -inf)."""
+    rng = np.random.default_rng(86)
+    N = 2512
+    q, k, v, s, g, c = make(rng, N, 16, 8, 128, "bf16")
+    s[:1600] = -np.inf
+    o, lse = gpu_split(q, k, v, s, g, c)
+    assert torch.all(o[:1600].float() == 0)
+    assert torch.all(torch.isneginf(lse[:, :1600]))
+    ro, rl = ref(q[1600:], k[1600:], v[1600:], s[1600:], g, c[1600:], "bf16")
+    assert_close_abs(as_f64(o)[1600:], ro, BF16_ABS, "attn_split_masked_rest")
+    assert_close_abs(lse.cpu().numpy()[:, 1600:], rl, LSE_ABS_BF16, "attn_split_masked_lse")
+
+
+def test_attn_split_all_masked():
+    rng = np.random.default_rng(87)
+    q, k, v, s, g, c = make(rng, 2512, 16, 8, 128, "bf16")
+    s[:] = -np.inf
+    o, lse = gpu_split(q, k, v, s, g, c)
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_attn_split_matches_unsplit_and_is_deterministic():
+    rng = np.random.default_rng(88)
+    q, k, v, s, g, c = make(rng, 2512, 16, 8, 128, "bf16")
+    o1, l1 = gpu_split(q, k, v, s, g, c)
+    o2, l2 = gpu_split(q, k, v, s, g, c)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    o3, l3 = gpu(q, k, v, s, g, c, "bf16")
+    assert_close_abs(as_f64(o1), as_f64(o3), BF16_ABS, "attn_split_vs_unsplit")
+    # the first 64 queries see one key tile: the same arithmetic either way
+    assert torch.equal(o1[:64].view(torch.int16), o3[:64].view(torch.int16))
+
+
+def test_attn_split_workspace_unused_shape_runs_unsplit():
+    """A shape the split does not apply to accepts a NULL workspace and
+    matches tg_bias_attn_fwd bit for bit."""
+    rng = np.random.default_rng(89)
+    q, k, v, s, g, c = make(rng, 100, 16, 8, 128, "bf16")
+    assert tg.tg_bias_attn_workspace_size(100, 16, 8, 128) == 0
+    o1, l1 = tg.tg_bias_attn_fwd_ws(to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16"),
+                                    to_dev(s), to_dev(g), None, to_dev(c))
+    o2, l2 = gpu(q, k, v, s, g, c, "bf16")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+
+
+def test_attn_bf16_t16k_full_split():
+    """The 16k prompt's kept set through the split path: every output row."""
+    w = workloads.get("t16k")
+    _, a = workloads.generate(w)
+    rng = np.random.default_rng(92)
+    s = rng.standard_normal(w.n_kept).astype(np.float32)
+    o, lse = gpu_split(a.q, a.k, a.v, s, a.gain, None)
+    ro, rl = ref(a.q, a.k, a.v, s, a.gain, None, "bf16")
+    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_t16k_full_split")
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_bf16_t16k_full_split_lse")

@@ -15,7 +15,7 @@ from gpu_util import report, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def make_case(w, packed, kv_layers=0):
+def make_case(w, packed, kv_layers=0, split=False):
     g, a = workloads.generate(w)
     dt = w.dtype
     c = dict(resid=to_dev(g.resid, dt), prunable=to_dev(g.prunable), w2=to_dev(g.w2),
@@ -33,6 +33,10 @@ def make_case(w, packed, kv_layers=0):
              score_kept=torch.empty(N, dtype=torch.float32, device=dev),
              out=torch.empty_like(c["q"]),
              lse=torch.empty((w.Hq, N), dtype=torch.float32, device=dev))
+    if split:
+        nb = tg.tg_bias_attn_workspace_size(N, w.Hq, w.Hkv, w.D)
+        assert nb > 0
+        c["attn_workspace"] = torch.empty(nb, dtype=torch.uint8, device=dev)
     if kv_layers:
         gen = torch.Generator(device=dev).manual_seed(21)
         for n in ("kv_k_cache", "kv_v_cache"):
@@ -66,8 +70,12 @@ def eager(c, w, packed):
     if "kv_k_cache" in c:
         tg.tg_kv_gather(c["kept_idx"], w.n_kept, c["kv_k_cache"], c["kv_v_cache"],
                         c["kv_k_kept"], c["kv_v_kept"])
-    tg.tg_bias_attn_fwd(c["q"], c["k"], c["v"], c["score_kept"], c["gain"], out=c["out"],
-                        lse=c["lse"])
+    if "attn_workspace" in c:
+        tg.tg_bias_attn_fwd_ws(c["q"], c["k"], c["v"], c["score_kept"], c["gain"],
+                               c["attn_workspace"], out=c["out"], lse=c["lse"])
+    else:
+        tg.tg_bias_attn_fwd(c["q"], c["k"], c["v"], c["score_kept"], c["gain"], out=c["out"],
+                            lse=c["lse"])
     torch.cuda.synchronize()
     return {n: c[n].clone() for n in outs(c)}
 
@@ -91,22 +99,23 @@ def same(c, ref, what):
 
 
 CASES = [
-    ("tiny", False, 0),
-    ("t16k", True, 0),
-    ("t16k", False, 0),
-    ("t16k", True, 2),    # with the lower layers' KV gather on a forked stream
-    ("multi", True, 0),   # T > 32768: the multi-workgroup top-K and its workspace
+    ("tiny", False, 0, False),
+    ("t16k", True, 0, False),
+    ("t16k", False, 0, False),
+    ("t16k", True, 2, False),    # with the lower layers' KV gather on a forked stream
+    ("t16k", True, 2, True),     # and the split-key attention with its workspace
+    ("multi", True, 0, False),   # T > 32768: the multi-workgroup top-K and its workspace
 ]
 
 
-@pytest.mark.parametrize("name,packed,kv_layers", CASES)
-def test_graph_replays_match_eager(name, packed, kv_layers):
+@pytest.mark.parametrize("name,packed,kv_layers,split", CASES)
+def test_graph_replays_match_eager(name, packed, kv_layers, split):
     if name == "multi":
         w = replace(workloads.get("t16k"), name="graph-40k", seed=11, T=40000, d=512, h=128,
                     p_lo=100, p_hi=39900, K=700)
     else:
         w = workloads.get(name)
-    c = make_case(w, packed, kv_layers)
+    c = make_case(w, packed, kv_layers, split)
     ref = eager(c, w, packed)
     kv = {n: c[n] for n in ("kv_k_cache", "kv_v_cache", "kv_k_kept", "kv_v_kept") if n in c}
     chain = tg.tg_chain_create(
@@ -114,7 +123,8 @@ def test_graph_replays_match_eager(name, packed, kv_layers):
         eps=w.eps, w1_packed=packed, scores=c["scores"], K=w.K, kept_idx=c["kept_idx"],
         n_kept=c["n_kept"], workspace=c["workspace"], N=w.n_kept, resid_kept=c["resid_kept"],
         pos_kept=c["pos_kept"], score_kept=c["score_kept"], q=c["q"], k=c["k"], v=c["v"],
-        attn_key_score=c["score_kept"], gain=c["gain"], out=c["out"], lse=c["lse"], **kv)
+        attn_key_score=c["score_kept"], gain=c["gain"], out=c["out"], lse=c["lse"],
+        attn_workspace=c.get("attn_workspace"), **kv)
     for rep in range(3):
         clobber(c)                     # eager work between replays
         torch.cuda.synchronize()
@@ -134,4 +144,5 @@ def test_graph_replays_match_eager(name, packed, kv_layers):
     torch.cuda.synchronize()
     same(c, ref2, name + " refilled")
     chain.close()
-    report("graph_chain_" + name, packed=packed, kv_layers=kv_layers, replays=5, bit_exact=True)
+    report("graph_chain_" + name, packed=packed, kv_layers=kv_layers, split=split, replays=5,
+           bit_exact=True)
