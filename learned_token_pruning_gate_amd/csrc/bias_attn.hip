@@ -631,9 +631,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 // cost of a whole CU's LDS per workgroup: they pay off while the grid is too
 // small to keep every CU busy with one-stream workgroups for several rounds.
 constexpr int64_t kTwoStreamMaxGrid = 1024;
-// Workgroups of the one-stream head-dim <= 128 kernel resident at once on
-// the chip (256 CUs, two per CU); two-stream workgroups take a whole CU.
-constexpr int kSlots1 = 512, kSlots2 = 256;
+// Workgroups resident at once on the chip (256 CUs): two per CU for the
+// one-stream kernel at head dim <= 128, one per CU for two-stream workgroups
+// and at head dim 256 (whose tile pair fills a CU's LDS).
+constexpr int kCUs = 256;
 constexpr int kMinChunkTiles = 4;
 // Cost model, in units of one key tile of one workgroup (~2.4 us at head
 // dim 128 with two workgroups per CU): each item adds its setup (Q and first
@@ -683,7 +684,7 @@ double list_schedule(const std::vector<double>& tasks, int slots) {
 
 SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal) {
   SplitPlan best_plan;
-  if (N <= 0 || D > 128) return best_plan;   // head dim 256 keeps one workgroup per CU
+  if (N <= 0) return best_plan;
   const int64_t G = Hq / Hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
   const int PB = 32 * (4 / hpw);
@@ -691,14 +692,18 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
   if (static_cast<int64_t>(npb) * nhg > kTwoStreamMaxGrid) return best_plan;
   const int n = static_cast<int>(N);
   const int nt_max = row_tiles(npb - 1, PB, n, causal);
-  const int max_bins = std::min(kMaxBins, kSlots1 / nhg);
+  const int slots = D <= 128 ? 2 * kCUs : kCUs;   // split workgroups resident at once
+  const int max_bins = std::min(kMaxBins, slots / nhg);
   if (max_bins < 1) return best_plan;
-  // unsplit: two key streams per workgroup, each walking half of its row
+  // unsplit: at head dim <= 128 two key streams per workgroup, each walking
+  // half of its row, one workgroup per CU; at 256 one stream
   std::vector<double> tasks;
   for (int p = npb - 1; p >= 0; --p)
-    for (int h = 0; h < nhg; ++h)
-      tasks.push_back((row_tiles(p, PB, n, causal) + 1) / 2 * kTwoStreamRoundUnits + kItemUnits);
-  double best = list_schedule(tasks, kSlots2) * kSplitGain;
+    for (int h = 0; h < nhg; ++h) {
+      const int nt = row_tiles(p, PB, n, causal);
+      tasks.push_back((D <= 128 ? (nt + 1) / 2 * kTwoStreamRoundUnits : nt) + kItemUnits);
+    }
+  double best = list_schedule(tasks, kCUs) * kSplitGain;
   const size_t state_bytes = static_cast<size_t>(4) * ((D / 32) * 16 * 64 + 128) * sizeof(float);
   struct Item {
     int size, p, c;
@@ -762,9 +767,9 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
     }
   }
   if (best_plan.ctiles == 0) return best_plan;
-  const size_t slots = static_cast<size_t>(best_plan.n_split_rows) * best_plan.nchunk * nhg;
-  best_plan.part_o_floats = slots * 4 * (D / 32) * 16 * 64;
-  best_plan.bytes = slots * state_bytes;
+  const size_t n_states = static_cast<size_t>(best_plan.n_split_rows) * best_plan.nchunk * nhg;
+  best_plan.part_o_floats = n_states * 4 * (D / 32) * 16 * 64;
+  best_plan.bytes = n_states * state_bytes;
   return best_plan;
 }
 
@@ -803,7 +808,7 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
   const int32_t npb = (a.N + PB - 1) / PB;
   const int32_t nhg = a.Hq / HPW;
   const NoSplit none{};
-  if constexpr (D <= 128) {
+  {
     if (pl.ctiles > 0 && workspace != nullptr) {
       SplitLaunch sl{};
       sl.a.part_o = static_cast<float*>(workspace);

@@ -225,6 +225,10 @@ SPLIT_SHAPES = [  # N, Hq, Hkv, D, causal: each takes the split (3 to 7 chunks p
     (2999, 8, 8, 128, True),                               # ragged last query block
     (4000, 8, 8, 128, True),
     (2000, 16, 8, 64, True),
+    # head dim 256: one workgroup per CU
+    (2512, 8, 2, 256, True), (2512, 8, 2, 256, False),
+    (1000, 4, 2, 256, True),
+    (700, 6, 2, 256, True),
 ]
 
 
