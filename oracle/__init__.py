@@ -66,6 +66,9 @@ def _bind(path):
     lib.tgo_bias_attn.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, D,
                                   ctypes.c_int, P, I64, P, P]
     lib.tgo_bias_attn.restype = None
+    lib.tgo_bias_attn_bwd.argtypes = [I64, I64, I64, I64, P, P, P, P, P, P, D, ctypes.c_int,
+                                      P, P, P, P, P, P]
+    lib.tgo_bias_attn_bwd.restype = None
     lib.tgo_num_threads.argtypes = []
     lib.tgo_num_threads.restype = ctypes.c_int
     return lib
@@ -190,6 +193,28 @@ class Oracle:
         return out, lse
 
 
+    def bias_attn_bwd(self, q, k, v, key_score, gain, dout, q_scale=None, scale=None,
+                      causal=True):
+        """(dq [N,Hq,D], dk [N,Hkv,D], dv [N,Hkv,D], dscore [N], dgain [Hq]),
+        fp64: gradients of sum(out * dout) for the forward of bias_attn."""
+        q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+        N, Hq, D = q.shape
+        Hkv = k.shape[1]
+        assert k.shape == (N, Hkv, D) and v.shape == (N, Hkv, D) and dout.shape == q.shape
+        assert Hkv > 0 and Hq % Hkv == 0
+        key_score, gain, q_scale = _f64(key_score), _f64(gain), _f64(q_scale)
+        assert key_score.shape == (N,) and gain.shape == (Hq,)
+        if scale is None or scale <= 0:
+            scale = 1.0 / np.sqrt(D)
+        dq = np.empty((N, Hq, D)); dk = np.empty((N, Hkv, D)); dv = np.empty((N, Hkv, D))
+        dscore = np.empty(N); dgain = np.empty(Hq)
+        self._lib.tgo_bias_attn_bwd(N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(key_score),
+                                    _ptr(gain), _ptr(q_scale), float(scale),
+                                    1 if causal else 0, _ptr(dout), _ptr(dq), _ptr(dk),
+                                    _ptr(dv), _ptr(dscore), _ptr(dgain))
+        return dq, dk, dv, dscore, dgain
+
+
 _default = None
 
 
@@ -222,3 +247,7 @@ def kv_gather(*args, **kwargs):
 
 def bias_attn(*args, **kwargs):
     return default().bias_attn(*args, **kwargs)
+
+
+def bias_attn_bwd(*args, **kwargs):
+    return default().bias_attn_bwd(*args, **kwargs)

@@ -210,3 +210,90 @@ void tgo_bias_attn(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
     free(z);
   }
 }
+
+/* ---------------------------------------------------------------------- */
+/* Token-gated attention backward: the gradients of sum(O * dO) with      */
+/* respect to Q, K, V, the key scores and the per-head gains.             */
+/*   P = softmax_c(z), z[c] = c_r (alpha <q_r, k_c> + g_h s_c)            */
+/*   dP[c] = <dO_r, v_c>,  Delta = sum_c P[c] dP[c]                       */
+/*   dZ[c] = P[c] (dP[c] - Delta)                                         */
+/*   dq_r += dZ c_r alpha k_c,  dk_c += dZ c_r alpha q_r,  dv_c += P dO_r */
+/*   dscore_c += dZ c_r g_h,    dgain_h += dZ c_r s_c                     */
+/* A key with P = 0 (masked or outside the causal range) contributes      */
+/* nothing, also to dgain where its score may be -inf.                    */
+/* ---------------------------------------------------------------------- */
+void tgo_bias_attn_bwd(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
+                       const double* q, const double* k, const double* v,
+                       const double* key_score, const double* gain,
+                       const double* q_scale, double scale, int causal,
+                       const double* dout, double* dq, double* dk, double* dv,
+                       double* dscore, double* dgain) {
+  const int64_t G = Hq / Hkv;
+  memset(dq, 0, (size_t)(N * Hq * D) * sizeof(double));
+  memset(dk, 0, (size_t)(N * Hkv * D) * sizeof(double));
+  memset(dv, 0, (size_t)(N * Hkv * D) * sizeof(double));
+  memset(dgain, 0, (size_t)Hq * sizeof(double));
+  /* per KV head: its keys' dk/dv are written by that head's query heads only */
+  double* ds_part = (double*)calloc((size_t)(Hkv * (N > 0 ? N : 1)), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t kvh = 0; kvh < Hkv; ++kvh) {
+    double* P = (double*)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    double* dZ = (double*)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+    for (int64_t hq = kvh * G; hq < (kvh + 1) * G; ++hq) {
+      double dg = 0.0;
+      for (int64_t r = 0; r < N; ++r) {
+        const double c_r = q_scale ? q_scale[r] : 1.0;
+        const double* q_r = q + (r * Hq + hq) * D;
+        const double* do_r = dout + (r * Hq + hq) * D;
+        const int64_t n_vis = causal ? (r + 1) : N;
+        double zmax = -INFINITY;
+        for (int64_t c = 0; c < n_vis; ++c) {
+          const double* k_c = k + (c * Hkv + kvh) * D;
+          double qk = 0.0;
+          for (int64_t e = 0; e < D; ++e) qk += q_r[e] * k_c[e];
+          P[c] = c_r * (scale * qk + key_score[c] * gain[hq]);
+          if (P[c] > zmax) zmax = P[c];
+        }
+        if (zmax == -INFINITY) continue; /* no visible key: no gradient */
+        double sum = 0.0;
+        for (int64_t c = 0; c < n_vis; ++c) {
+          P[c] = exp(P[c] - zmax);
+          sum += P[c];
+        }
+        double delta = 0.0;
+        for (int64_t c = 0; c < n_vis; ++c) {
+          P[c] /= sum;
+          const double* v_c = v + (c * Hkv + kvh) * D;
+          double dp = 0.0;
+          for (int64_t e = 0; e < D; ++e) dp += do_r[e] * v_c[e];
+          dZ[c] = dp;
+          delta += P[c] * dp;
+        }
+        double* dq_r = dq + (r * Hq + hq) * D;
+        for (int64_t c = 0; c < n_vis; ++c) {
+          if (P[c] == 0.0) continue;
+          const double dz = P[c] * (dZ[c] - delta);
+          const double* k_c = k + (c * Hkv + kvh) * D;
+          double* dk_c = dk + (c * Hkv + kvh) * D;
+          double* dv_c = dv + (c * Hkv + kvh) * D;
+          for (int64_t e = 0; e < D; ++e) {
+            dq_r[e] += dz * c_r * scale * k_c[e];
+            dk_c[e] += dz * c_r * scale * q_r[e];
+            dv_c[e] += P[c] * do_r[e];
+          }
+          ds_part[kvh * N + c] += dz * c_r * gain[hq];
+          dg += dz * c_r * key_score[c];
+        }
+      }
+      dgain[hq] = dg;
+    }
+    free(P);
+    free(dZ);
+  }
+  for (int64_t c = 0; c < N; ++c) {
+    double acc = 0.0;
+    for (int64_t kvh = 0; kvh < Hkv; ++kvh) acc += ds_part[kvh * N + c];
+    dscore[c] = acc;
+  }
+  free(ds_part);
+}

@@ -84,6 +84,20 @@ void tgo_bias_attn(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
                    double* lse);
 
 /* Number of threads the OpenMP loops above use (1 without OpenMP). */
+/* Gradients of token-gated attention (TokenGate pages: ai.info summary "Key
+ * Contributions" items 2 and 3 -- the gate is trained end to end through the
+ * attention bias, which needs the gradient of the logits with respect to the
+ * key scores and the per-head gains).  With the forward of tgo_bias_attn and
+ * an upstream gradient dout [N][Hq][D], writes dq [N][Hq][D], dk, dv
+ * [N][Hkv][D], dscore [N] and dgain [Hq], all fp64.  Recomputes the
+ * softmax from its definition. */
+void tgo_bias_attn_bwd(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
+                       const double* q, const double* k, const double* v,
+                       const double* key_score, const double* gain,
+                       const double* q_scale, double scale, int causal,
+                       const double* dout, double* dq, double* dk, double* dv,
+                       double* dscore, double* dgain);
+
 int tgo_num_threads(void);
 
 #ifdef __cplusplus

@@ -486,4 +486,102 @@ def pin_attn_rows_subset(orc):
     assert np.array_equal(sub, full[rows]) and np.array_equal(ls, lf[:, rows])
 
 
+# ---------------------------------------------------------------------------
+# attention backward
+# ---------------------------------------------------------------------------
+def torch_bias_attn_grads(q, k, v, key_score, gain, q_scale, scale, causal, dout):
+    """fp64 torch autograd through an explicit masked softmax: gradients of
+    sum(O * dout) for q, k, v, key_score, gain."""
+    t = lambda a: torch.tensor(np.asarray(a, np.float64), requires_grad=True)
+    q, k, v, s, g = t(q), t(k), t(v), t(key_score), t(gain)
+    N, Hq, D = q.shape
+    G = Hq // k.shape[1]
+    c = torch.ones(N, dtype=torch.float64) if q_scale is None else \
+        torch.from_numpy(np.asarray(q_scale, np.float64))
+    kh = k.repeat_interleave(G, dim=1)                          # [N, Hq, D]
+    vh = v.repeat_interleave(G, dim=1)
+    dots = torch.einsum("rhe,che->hrc", q, kh)                  # [Hq, N, N]
+    z = c[None, :, None] * (scale * dots + g[:, None, None] * s[None, None, :])
+    if causal:
+        upper = torch.triu(torch.ones(N, N, dtype=torch.bool), diagonal=1)
+        z = z.masked_fill(upper[None], float("-inf"))
+    p = torch.softmax(z, dim=-1)
+    o = torch.einsum("hrc,che->rhe", p, vh)
+    (o * torch.from_numpy(np.asarray(dout, np.float64))).sum().backward()
+    return [x.grad.numpy() for x in (q, k, v, s, g)]
+
+
+def pin_attn_bwd_torch_autograd(orc):
+    rng = np.random.default_rng(31)
+    for N, Hq, Hkv, D, causal, scaled in [(1, 2, 1, 4, True, True),
+                                          (23, 4, 2, 8, True, True),
+                                          (19, 4, 4, 16, True, False),
+                                          (21, 6, 2, 8, False, True)]:
+        q, k, v, s, g, c = _attn_case(rng, N, Hq, Hkv, D, scaled)
+        do = rng.standard_normal((N, Hq, D))
+        scale = 1.0 / math.sqrt(D)
+        got = orc.bias_attn_bwd(q, k, v, s, g, do, q_scale=c, causal=causal)
+        ref = torch_bias_attn_grads(q, k, v, s, g, c, scale, causal, do)
+        for name, a, b in zip(("dq", "dk", "dv", "dscore", "dgain"), got, ref):
+            _close(a, b, 1e-10, 1e-12, "attn bwd %s N=%d causal=%d" % (name, N, causal))
+
+
+def pin_attn_bwd_finite_differences(orc):
+    """Central differences of sum(O * dO) through the oracle's forward."""
+    rng = np.random.default_rng(32)
+    N, Hq, Hkv, D = 6, 4, 2, 3
+    q, k, v, s, g, c = _attn_case(rng, N, Hq, Hkv, D)
+    do = rng.standard_normal((N, Hq, D))
+    scale = 0.6
+    dq, dk, dv, ds, dg = orc.bias_attn_bwd(q, k, v, s, g, do, q_scale=c, scale=scale)
+
+    def loss(q_, k_, v_, s_, g_):
+        o, _ = orc.bias_attn(q_, k_, v_, s_, g_, q_scale=c, scale=scale)
+        return float(np.sum(o * do))
+
+    eps = 1e-6
+    base = [q, k, v, s, g]
+    grads = [dq, dk, dv, ds, dg]
+    picks = [(0, (3, 1, 0)), (0, (5, 2, 2)), (1, (1, 0, 2)), (1, (4, 1, 1)), (2, (2, 1, 0)),
+             (2, (0, 0, 1)), (3, (2,)), (3, (5,)), (4, (0,)), (4, (3,))]
+    for which, idx in picks:
+        plus = [x.copy() for x in base]
+        minus = [x.copy() for x in base]
+        plus[which][idx] += eps
+        minus[which][idx] -= eps
+        fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+        an = grads[which][idx]
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, idx, fd, an)
+
+
+def pin_attn_bwd_invariants(orc):
+    rng = np.random.default_rng(33)
+    N, Hq, Hkv, D = 30, 4, 2, 8
+    q, k, v, s, g, c = _attn_case(rng, N, Hq, Hkv, D)
+    do = rng.standard_normal((N, Hq, D))
+    dq, dk, dv, ds, dg = orc.bias_attn_bwd(q, k, v, s, g, do, q_scale=c)
+    # adding a constant to every score of a row leaves the softmax unchanged
+    assert abs(ds.sum()) <= 1e-10 * np.abs(ds).sum()
+    # a key-constant score: dgain_h = kappa * sum of each row's dZ = 0
+    _, _, _, _, dg0 = orc.bias_attn_bwd(q, k, v, np.full(N, 1.7), g, do, q_scale=c)
+    assert np.all(np.abs(dg0) <= 1e-10 * (1.0 + np.abs(dg).max()))
+    # no upstream gradient, no gradient
+    for a in orc.bias_attn_bwd(q, k, v, s, g, np.zeros_like(do), q_scale=c):
+        assert np.all(a == 0.0)
+    # a -inf score deletes its key: zero gradients for it; with row 7's own
+    # upstream gradient zeroed too, the rest equals the problem without token 7
+    s2 = s.copy()
+    s2[7] = -np.inf
+    do2 = do.copy()
+    do2[7] = 0.0
+    dq2, dk2, dv2, ds2, dg2 = orc.bias_attn_bwd(q, k, v, s2, g, do2, q_scale=c)
+    assert np.all(dk2[7] == 0) and np.all(dv2[7] == 0) and ds2[7] == 0 and np.all(np.isfinite(dg2))
+    keep = np.array([i for i in range(N) if i != 7])
+    r = orc.bias_attn_bwd(q[keep], k[keep], v[keep], s[keep], g, do[keep], q_scale=c[keep])
+    _close(dq2[keep], r[0], 1e-12, 1e-12, "bwd delete dq")
+    _close(dk2[keep], r[1], 1e-12, 1e-12, "bwd delete dk")
+    _close(ds2[keep], r[3], 1e-12, 1e-12, "bwd delete dscore")
+    _close(dg2, r[4], 1e-12, 1e-12, "bwd delete dgain")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -56,6 +56,16 @@ MUTANTS = [
     ("attn_no_normalise", "for (int64_t e = 0; e < D; ++e) o[e] /= denom;", ";"),
     ("attn_q_by_kv_head", "const double* qr = q + (r * Hq + hq) * D;", "const double* qr = q + (r * Hq + kv) * D;"),
     ("attn_v_from_first_head", "const double* vc = v + (c * Hkv + kv) * D;", "const double* vc = v + (c * Hkv) * D;"),
+    ("bwd_delta_sign", "P[c] * (dZ[c] - delta)", "P[c] * (dZ[c] + delta)"),
+    ("bwd_dq_no_qscale", "dq_r[e] += dz * c_r * scale * k_c[e];", "dq_r[e] += dz * scale * k_c[e];"),
+    ("bwd_dk_no_scale", "dk_c[e] += dz * c_r * scale * q_r[e];", "dk_c[e] += dz * c_r * q_r[e];"),
+    ("bwd_dv_uses_dz", "dv_c[e] += P[c] * do_r[e];", "dv_c[e] += dz * do_r[e];"),
+    ("bwd_dscore_no_gain", "ds_part[kvh * N + c] += dz * c_r * gain[hq];",
+     "ds_part[kvh * N + c] += dz * c_r;"),
+    ("bwd_dgain_no_qscale", "dg += dz * c_r * key_score[c];", "dg += dz * key_score[c];"),
+    ("bwd_causal_excludes_diag", "causal ? (r + 1) : N", "causal ? r : N"),
+    ("bwd_no_normalise", "P[c] /= sum;", "(void)sum;"),
+    ("bwd_dk_from_first_head", "double* dk_c = dk + (c * Hkv + kvh) * D;", "double* dk_c = dk + (c * Hkv) * D;"),
 ]
 
 RUNNER = r"""
