@@ -266,6 +266,49 @@ tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
                               size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * Token-gated attention, backward.  Pages: ai.info summary "Key
+ * Contributions" items 2 and 3: the gate is trained end to end, and its
+ * scores reach the loss only through the per-key bias gain_h * score_c, so
+ * training needs the gradients of the biased attention with respect to the
+ * scores and the gains as well as Q, K and V.
+ *
+ * With the forward of tg_bias_attn_fwd (same arguments) and an upstream
+ * gradient dO, for z[h,r,c] = c_r (alpha <q_r,k_c> + gain_h score_c):
+ *   dZ = P (dO V^T - <dO, O>)           (P the forward's softmax)
+ *   dQ = c alpha dZ K,  dK = sum_h (c alpha dZ)^T Q,  dV = sum_h P^T dO
+ *   dscore[c] = sum_{h,r} gain_h c_r dZ[h,r,c]
+ *   dgain[h]  = sum_{r,c} score_c c_r dZ[h,r,c]   (keys with P = 0 add 0)
+ *
+ * dt            TG_DTYPE_BF16 only (TG_ERR_UNSUPPORTED otherwise).
+ * D             64 or 128 (TG_ERR_UNSUPPORTED otherwise).
+ * q, k, v, key_score, gain, q_scale, softmax_scale, causal
+ *               as given to tg_bias_attn_fwd.
+ * out, lse      the forward's outputs: out [N][Hq][D] bf16 and lse [Hq][N]
+ *               f32 (both required).
+ * dout          [N][Hq][D] bf16, the gradient of the loss w.r.t. out.
+ * dq            out, [N][Hq][D] bf16.  dk, dv: out, [N][Hkv][D] bf16.
+ * dscore        out, [N] f32; dgain: out, [Hq] f32.  Required when
+ *               key_score != NULL, ignored (not written) when it is NULL.
+ * workspace     device memory of at least tg_bias_attn_bwd_workspace_size
+ *               bytes, 16-byte aligned; needs no initialisation.  Calls
+ *               sharing it must be ordered on one stream.
+ * All tensors 16-byte aligned.  Results are deterministic (fixed-order
+ * reductions, no atomics).  Errors: TG_ERR_INVALID_ARGUMENT,
+ * TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, with nothing enqueued.
+ * ------------------------------------------------------------------------ */
+size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv);
+
+tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
+                           int64_t D, const void* q, const void* k,
+                           const void* v, const float* key_score,
+                           const float* gain, const float* q_scale,
+                           float softmax_scale, int causal, const void* out,
+                           const void* dout, const float* lse, void* dq,
+                           void* dk, void* dv, float* dscore, float* dgain,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* --------------------------------------------------------------------------
  * Lower layers' KV cache gathered to the kept tokens.  Pages: ai.info summary
  * "Key Contributions" item 1 (layers above the gate never create KV entries
  * for pruned tokens) and "Methodology in Plain English" (the layers below

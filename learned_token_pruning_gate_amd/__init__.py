@@ -17,6 +17,8 @@ Entry points (same names as the C ABI):
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
 * ``tg_bias_attn_workspace_size`` / ``tg_bias_attn_fwd_ws`` -- the same with
                           long rows' keys split over workgroups (short prompts)
+* ``tg_bias_attn_bwd_workspace_size`` / ``tg_bias_attn_bwd`` -- its gradients
+                          (dQ, dK, dV, dscore, dgain)
 * ``tg_kv_gather``        -- lower layers' KV cache gathered to the kept tokens
 * ``tg_chain_create`` / ``TgChain.launch`` -- the four calls captured once as
                           a HIP graph and replayed
@@ -33,7 +35,8 @@ __all__ = [
     "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
     "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
     "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_bias_attn_workspace_size",
-    "tg_bias_attn_fwd_ws", "tg_kv_gather", "tg_chain_create", "TgChain",
+    "tg_bias_attn_fwd_ws", "tg_bias_attn_bwd_workspace_size", "tg_bias_attn_bwd",
+    "tg_kv_gather", "tg_chain_create", "TgChain",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
     "TG_ERR_LAUNCH", "TG_DTYPE_F32", "TG_DTYPE_BF16",
 ]
@@ -47,7 +50,8 @@ TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
             "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
             "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
-            "tg_bias_attn_workspace_size", "tg_bias_attn_fwd_ws", "tg_kv_gather",
+            "tg_bias_attn_workspace_size", "tg_bias_attn_fwd_ws",
+            "tg_bias_attn_bwd_workspace_size", "tg_bias_attn_bwd", "tg_kv_gather",
             "tg_chain_create",
             "tg_chain_launch", "tg_chain_destroy")
 
@@ -116,6 +120,11 @@ def load():
     lib.tg_bias_attn_fwd_ws.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P,
                                         ctypes.c_size_t, P]
     lib.tg_bias_attn_fwd_ws.restype = I
+    lib.tg_bias_attn_bwd_workspace_size.argtypes = [I64, I64, I64]
+    lib.tg_bias_attn_bwd_workspace_size.restype = ctypes.c_size_t
+    lib.tg_bias_attn_bwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P, P, P,
+                                     P, P, P, P, ctypes.c_size_t, P]
+    lib.tg_bias_attn_bwd.restype = I
     lib.tg_kv_gather.argtypes = [I, I64, I64, I64, I64, I64, P, P, P, P, P, P]
     lib.tg_kv_gather.restype = I
     lib.tg_chain_create.argtypes = [ctypes.POINTER(ChainDesc), ctypes.POINTER(P)]
@@ -428,6 +437,44 @@ def tg_bias_attn_fwd_ws(q, k, v, key_score, gain, workspace, q_scale=None, softm
     tg_bias_attn_workspace_size bytes, or None)."""
     return _bias_attn(q, k, v, key_score, gain, q_scale, softmax_scale, causal, out, lse,
                       want_lse, stream, True, workspace)
+
+
+def tg_bias_attn_bwd_workspace_size(N: int, Hq: int, Hkv: int) -> int:
+    return int(load().tg_bias_attn_bwd_workspace_size(int(N), int(Hq), int(Hkv)))
+
+
+def tg_bias_attn_bwd(q, k, v, key_score, gain, out, dout, lse, q_scale=None, softmax_scale=0.0,
+                     causal=True, workspace=None, stream=None):
+    """(dq, dk, dv, dscore, dgain); dscore/dgain are None without key_score."""
+    lib = load()
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out"), (dout, "dout")):
+        _dev(t, n, q.dtype)
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % n)
+    N, Hq, D = q.shape
+    Hkv = k.shape[1]
+    if tuple(out.shape) != (N, Hq, D) or tuple(dout.shape) != (N, Hq, D):
+        raise ValueError("out and dout must be [N, Hq, D]")
+    _dev(lse, "lse", torch.float32)
+    _dev(key_score, "key_score", torch.float32, allow_none=True)
+    _dev(gain, "gain", torch.float32, allow_none=True)
+    _dev(q_scale, "q_scale", torch.float32, allow_none=True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dscore = dgain = None
+    if key_score is not None:
+        dscore = torch.empty(N, dtype=torch.float32, device=q.device)
+        dgain = torch.empty(Hq, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(tg_bias_attn_bwd_workspace_size(N, Hq, Hkv), 16),
+                                dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    st = lib.tg_bias_attn_bwd(_dt(q), N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(key_score),
+                              _ptr(gain), _ptr(q_scale), float(softmax_scale),
+                              1 if causal else 0, _ptr(out), _ptr(dout), _ptr(lse), _ptr(dq),
+                              _ptr(dk), _ptr(dv), _ptr(dscore), _ptr(dgain), _ptr(workspace),
+                              workspace.numel(), _stream(stream))
+    _check(st, "tg_bias_attn_bwd")
+    return dq, dk, dv, dscore, dgain
 
 
 def tg_bias_attn_fwd(q, k, v, key_score, gain, q_scale=None, softmax_scale=0.0, causal=True,

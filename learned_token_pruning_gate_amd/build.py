@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "compact_gather.hip", "topk_select.hip", "gate_score.hip",
-           "bias_attn.hip", "kv_gather.hip", "chain.cpp"]
+           "bias_attn.hip", "bias_attn_bwd.hip", "kv_gather.hip", "chain.cpp"]
 
 CFLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-Wall", "-Wno-unused-function",

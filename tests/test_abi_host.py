@@ -220,6 +220,36 @@ def test_attn_ws_validation(lib):
     assert _attn_ws(lib, FAKE, 0, N=0) == OK            # nothing to do, nothing needed
 
 
+def _bwd(lib, ws=FAKE, nbytes=1 << 30, dt=BF16, N=64, Hq=4, Hkv=2, D=128, q=FAKE, ks=FAKE,
+         dscore=FAKE, lse=FAKE):
+    return lib.tg_bias_attn_bwd(dt, N, Hq, Hkv, D, q, FAKE, FAKE, ks, FAKE, None,
+                                ctypes.c_float(0.0), 1, FAKE, FAKE, lse, FAKE, FAKE, FAKE,
+                                dscore, FAKE, ws, nbytes, None)
+
+
+def test_attn_bwd_workspace_size(lib):
+    # Delta and lse2 [Hq][N], dscore partials [Hkv][N], dgain partials
+    # [ceil(N/128) x 4 waves][Hq], all f32
+    assert lib.tg_bias_attn_bwd_workspace_size(2512, 16, 8) == \
+        (2 * 16 * 2512 + 8 * 2512 + 20 * 4 * 16) * 4
+    assert lib.tg_bias_attn_bwd_workspace_size(0, 16, 8) == 0
+    assert lib.tg_bias_attn_bwd_workspace_size(100, 6, 4) == 0   # Hq % Hkv != 0
+
+
+def test_attn_bwd_validation(lib):
+    assert _bwd(lib, dt=3) == INVAL
+    assert _bwd(lib, dt=F32) == UNSUP
+    assert _bwd(lib, D=256) == UNSUP
+    assert _bwd(lib, Hq=6, Hkv=4) == INVAL
+    assert _bwd(lib, ws=None, nbytes=0) == WS
+    assert _bwd(lib, nbytes=16) == WS
+    assert _bwd(lib, ws=FAKE_ODD) == INVAL
+    assert _bwd(lib, q=None) == INVAL
+    assert _bwd(lib, lse=None) == INVAL
+    assert _bwd(lib, dscore=None) == INVAL          # scores given, no dscore output
+    assert _bwd(lib, N=0, ws=None, nbytes=0) == OK
+
+
 def test_product_binding_refuses_cpu_tensors():
     import torch
     import learned_token_pruning_gate_amd as tg
