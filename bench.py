@@ -151,6 +151,10 @@ def main():
                          "(tg_bias_attn_fwd_ws: long rows' keys cut into chunks on separate "
                          "workgroups, then merged) when the shape uses one; off runs "
                          "tg_bias_attn_fwd")
+    ap.add_argument("--no-attn-bwd", action="store_true",
+                    help="skip the separate timing of the attention backward "
+                         "(tg_bias_attn_bwd on the step's forward outputs; reported beside "
+                         "the step, not part of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel that "
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -351,6 +355,37 @@ def main():
     roof["kernel"] = dominant
     roof["traffic"] = load_traffic(dominant)
 
+    # attention backward (the gate's training path), timed on its own: not
+    # part of the prefill step
+    bwd_info = None
+    if dt == "bf16" and w.D in (64, 128) and not args.no_attn_bwd:
+        gen = torch.Generator(device=dev).manual_seed(17)
+        dout = torch.randn(q.shape, generator=gen, device=dev).to(q.dtype)
+        dq_, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        dscore_ = torch.empty(N, dtype=torch.float32, device=dev)
+        dgain_ = torch.empty(w.Hq, dtype=torch.float32, device=dev)
+        bws = torch.empty(max(tg.tg_bias_attn_bwd_workspace_size(N, w.Hq, w.Hkv), 16),
+                          dtype=torch.uint8, device=dev)
+        check(lib.tg_bias_attn_fwd_ws(*att_args), "tg_bias_attn_fwd_ws")   # out, lse
+        bwd_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), key_ptr, P(gain), P(q_scale),
+                    F(0.0), 1, P(out), P(dout), P(lse), P(dq_), P(dk_), P(dv_), P(dscore_),
+                    P(dgain_), P(bws), bws.numel(), sp)
+        for _ in range(2):
+            check(lib.tg_bias_attn_bwd(*bwd_args), "tg_bias_attn_bwd")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            check(lib.tg_bias_attn_bwd(*bwd_args), "tg_bias_attn_bwd")
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.steps
+        bwd_flops = 5 * w.D * w.Hq * N * (N + 1)   # S, dP, dV, dK, dQ products (causal)
+        bwd_info = {"ms": bwd_ms, "flops": bwd_flops,
+                    "TFLOP_s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
+                    "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                    "calls": args.steps}
+
     cold = None
     if args.cold:
         flush = torch.empty(1 << 29, dtype=torch.uint8, device=dev)  # 512 MiB > MALL
@@ -381,6 +416,7 @@ def main():
         "attn_frac_of_peak": stage_info["attn"].get("mfma_frac"),
         "roofline": roof,
         "stages": stage_info,
+        "attn_bwd": bwd_info,
     }
     if cold:
         result["cold_stage_ms"] = cold
