@@ -364,7 +364,7 @@ def main():
         dq_, dk_, dv_ = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         dscore_ = torch.empty(N, dtype=torch.float32, device=dev)
         dgain_ = torch.empty(w.Hq, dtype=torch.float32, device=dev)
-        bws = torch.empty(max(tg.tg_bias_attn_bwd_workspace_size(N, w.Hq, w.Hkv), 16),
+        bws = torch.empty(max(tg.tg_bias_attn_bwd_workspace_size(N, w.Hq, w.Hkv, w.D), 16),
                           dtype=torch.uint8, device=dev)
         check(lib.tg_bias_attn_fwd_ws(*att_args), "tg_bias_attn_fwd_ws")   # out, lse
         bwd_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), key_ptr, P(gain), P(q_scale),

@@ -290,13 +290,18 @@ tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
  * dscore        out, [N] f32; dgain: out, [Hq] f32.  Required when
  *               key_score != NULL, ignored (not written) when it is NULL.
  * workspace     device memory of at least tg_bias_attn_bwd_workspace_size
- *               bytes, 16-byte aligned; needs no initialisation.  Calls
- *               sharing it must be ordered on one stream.
+ *               bytes (0 for invalid shapes), 16-byte aligned; needs no
+ *               initialisation.  It holds Delta, the log-sum-exp in log2
+ *               units and the fp32 partial sums of the dK/dV workgroups,
+ *               which split each key block's query range into chunks when
+ *               the prompt is short.  Calls sharing it must be ordered on
+ *               one stream.
  * All tensors 16-byte aligned.  Results are deterministic (fixed-order
  * reductions, no atomics).  Errors: TG_ERR_INVALID_ARGUMENT,
  * TG_ERR_UNSUPPORTED, TG_ERR_WORKSPACE, with nothing enqueued.
  * ------------------------------------------------------------------------ */
-size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv);
+size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv,
+                                       int64_t D);
 
 tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
                            int64_t D, const void* q, const void* k,

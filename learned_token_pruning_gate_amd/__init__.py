@@ -120,7 +120,7 @@ def load():
     lib.tg_bias_attn_fwd_ws.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P,
                                         ctypes.c_size_t, P]
     lib.tg_bias_attn_fwd_ws.restype = I
-    lib.tg_bias_attn_bwd_workspace_size.argtypes = [I64, I64, I64]
+    lib.tg_bias_attn_bwd_workspace_size.argtypes = [I64, I64, I64, I64]
     lib.tg_bias_attn_bwd_workspace_size.restype = ctypes.c_size_t
     lib.tg_bias_attn_bwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P, P, P,
                                      P, P, P, P, ctypes.c_size_t, P]
@@ -439,8 +439,8 @@ def tg_bias_attn_fwd_ws(q, k, v, key_score, gain, workspace, q_scale=None, softm
                       want_lse, stream, True, workspace)
 
 
-def tg_bias_attn_bwd_workspace_size(N: int, Hq: int, Hkv: int) -> int:
-    return int(load().tg_bias_attn_bwd_workspace_size(int(N), int(Hq), int(Hkv)))
+def tg_bias_attn_bwd_workspace_size(N: int, Hq: int, Hkv: int, D: int) -> int:
+    return int(load().tg_bias_attn_bwd_workspace_size(int(N), int(Hq), int(Hkv), int(D)))
 
 
 def tg_bias_attn_bwd(q, k, v, key_score, gain, out, dout, lse, q_scale=None, softmax_scale=0.0,
@@ -465,7 +465,7 @@ def tg_bias_attn_bwd(q, k, v, key_score, gain, out, dout, lse, q_scale=None, sof
         dscore = torch.empty(N, dtype=torch.float32, device=q.device)
         dgain = torch.empty(Hq, dtype=torch.float32, device=q.device)
     if workspace is None:
-        workspace = torch.empty(max(tg_bias_attn_bwd_workspace_size(N, Hq, Hkv), 16),
+        workspace = torch.empty(max(tg_bias_attn_bwd_workspace_size(N, Hq, Hkv, D), 16),
                                 dtype=torch.uint8, device=q.device)
     _dev(workspace, "workspace", torch.uint8)
     st = lib.tg_bias_attn_bwd(_dt(q), N, Hq, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(key_score),

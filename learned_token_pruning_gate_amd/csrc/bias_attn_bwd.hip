@@ -26,6 +26,8 @@
 //     fixed order (deterministic).
 // bf16 inputs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dZ
 // are rounded to bf16 only as operands of the dV, dK and dQ products.
+#include <algorithm>
+
 #include "tg_common.hpp"
 
 namespace tg {
@@ -374,8 +376,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    float* __restrict__ part_ds, float* __restrict__ part_dg, int32_t N, int32_t Hq,
-    int32_t Hkv) {
+    float* __restrict__ part_kv, float* __restrict__ part_ds, float* __restrict__ part_dg,
+    int32_t N, int32_t Hq, int32_t Hkv, int32_t nkb, int32_t qchunk) {
   using St = Stage<D>;
   constexpr int DK = D / 16;
   constexpr int DB = D / 32;
@@ -383,9 +385,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+  // workgroup = (query chunk, key block, KV head), the KV head fastest; a key
+  // block's query tiles are cut into chunks of qchunk tiles
   const int kvh = blockIdx.x % Hkv;
-  const int kblock = blockIdx.x / Hkv;   // causal: lower key blocks see more queries, go first
+  const int kblock = (blockIdx.x / Hkv) % nkb;   // causal: lower key blocks see more queries
+  const int chunk = blockIdx.x / (Hkv * nkb);
   const int key0 = kblock * kKeysPerWg;
+  const int nq = (N + kTile - 1) / kTile;
+  const int t_lo = (CAUSAL ? key0 / kTile : 0) + chunk * qchunk;
+  if (t_lo >= nq) return;   // uniform: this key block has fewer chunks
+  // several chunks: dK/dV go to fp32 partials, summed by attn_bwd_kv_reduce_kernel
+  const bool split = (nq - (CAUSAL ? key0 / kTile : 0)) > qchunk;
+  const size_t slot = (static_cast<size_t>(chunk) * nkb + kblock) * Hkv + kvh;
   const int my_k = key0 + 32 * wave + l32;
   const bool k_ok = my_k < N;
   const int G = Hq / Hkv;
@@ -415,15 +426,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const bf16x8 ones = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
                                                          : u32x4{0, 0, 0, 0});
 
-  const int t_first = CAUSAL ? key0 / kTile : 0;
-  const int t_count = (N + kTile - 1) / kTile - t_first;   // query tiles per head
+  const int t_count = min(qchunk, nq - t_lo);   // query tiles per head
   const int n_iter = G * t_count;
 
   u32x4 qr[St::RI], dr[St::RI], qp[St::PPT][4], dpc[St::PPT][4];
   float vec_ac = 0.0f, vec_l2 = 0.0f, vec_dl = 0.0f;
   auto load_tile = [&](int it) {
     const int h = kvh * G + it / t_count;
-    const int q0 = (t_first + it % t_count) * kTile;
+    const int q0 = (t_lo + it % t_count) * kTile;
     const uint32_t hoff = static_cast<uint32_t>(h) * D * 2;
     St::load_rows(qr, q_rs, q_row, hoff, q0, tid);
     St::load_rows(dr, d_rs, q_row, hoff, q0, tid);
@@ -466,7 +476,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   for (int it = 0; it < n_iter; ++it) {
     const DkvSmem<D>& b = sm[it & 1];
     const int h = kvh * G + it / t_count;
-    const int q0 = (t_first + it % t_count) * kTile;
+    const int q0 = (t_lo + it % t_count) * kTile;
     const bool more = it + 1 < n_iter;
     if (it % t_count == 0) {   // a new head: its bias k-step on the key side
       u32x4 kb4 = u32x4{0, 0, 0, 0};
@@ -543,14 +553,29 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       float g_part = (k_ok && hh == 0 && s_key != -INFINITY) ? s_key * a_key : 0.0f;
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) g_part += __shfl_xor(g_part, m, 64);
-      if (lane == 0) part_dg[(static_cast<int64_t>(kblock) * 4 + wave) * Hq + h] = g_part;
+      if (lane == 0) part_dg[(slot * 4 + wave) * G + (h - kvh * G)] = g_part;
       a_sum = 0.0f;
     }
     if (more) store_tile(sm[(it + 1) & 1]);
     __syncthreads();
   }
 
-  if (k_ok) {
+  const int key_local = 32 * wave + l32;
+  if (HAS_BIAS && hh == 0) part_ds[slot * kKeysPerWg + key_local] = ds_sum;
+  if (split) {
+    // dK^T, dV^T accumulator entries of this lane: dims 32 db + 8 j + 4 hh .. +3
+    float* pk = part_kv + ((slot * 2) * kKeysPerWg + key_local) * D + 4 * hh;
+    float* pv = pk + static_cast<size_t>(kKeysPerWg) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *reinterpret_cast<f32x4*>(pk + 32 * db + 8 * j) =
+            f32x4{dka[db][4 * j], dka[db][4 * j + 1], dka[db][4 * j + 2], dka[db][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(pv + 32 * db + 8 * j) =
+            f32x4{dva[db][4 * j], dva[db][4 * j + 1], dva[db][4 * j + 2], dva[db][4 * j + 3]};
+      }
+  } else if (k_ok) {
     const int64_t off = static_cast<int64_t>(my_k) * Hkv * D + static_cast<int64_t>(kvh) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -565,42 +590,119 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
         *reinterpret_cast<bf16x4*>(dk + off + 32 * db + 8 * j + 4 * hh) = wk;
         *reinterpret_cast<bf16x4*>(dv + off + 32 * db + 8 * j + 4 * hh) = wv;
       }
-    if (HAS_BIAS && hh == 0) part_ds[static_cast<int64_t>(kvh) * N + my_k] = ds_sum;
   }
 }
 
-// dscore[c] = sum over KV heads of part_ds; dgain[h] = sum over key blocks
-// and waves of part_dg.  Fixed summation order: deterministic.
+// Chunks of a split key block (causal: key block kb's first query tile is
+// 2 kb; chunk count ceil(tiles / qchunk)).
+__device__ __forceinline__ int kv_chunks(int kb, int nq, int qchunk, bool causal) {
+  const int tiles = nq - (causal ? kb * (kKeysPerWg / kTile) : 0);
+  return (tiles + qchunk - 1) / qchunk;
+}
+
+// dK, dV of split key blocks: the chunks' fp32 partials summed in chunk
+// order, stored as bf16.  One thread per (key, KV head, 4 dims).
+template <int D>
+__global__ __launch_bounds__(256) void attn_bwd_kv_reduce_kernel(
+    const float* __restrict__ part_kv, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
+    int32_t N, int32_t Hkv, int32_t nkb, int32_t qchunk, int causal) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_key = static_cast<int64_t>(Hkv) * (D / 4);
+  if (i >= static_cast<int64_t>(N) * per_key) return;
+  const int key = static_cast<int>(i / per_key);
+  const int kvh = static_cast<int>((i % per_key) / (D / 4));
+  const int d4 = static_cast<int>(i % (D / 4));
+  const int kb = key / kKeysPerWg, kl = key % kKeysPerWg;
+  const int nq = (N + kTile - 1) / kTile;
+  const int nc = kv_chunks(kb, nq, qchunk, causal != 0);
+  if (nc <= 1) return;   // written directly by the key block's only workgroup
+  f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = sk;
+  for (int c = 0; c < nc; ++c) {
+    const size_t slot = (static_cast<size_t>(c) * nkb + kb) * Hkv + kvh;
+    const float* pk = part_kv + ((slot * 2) * kKeysPerWg + kl) * D + 4 * d4;
+    sk += *reinterpret_cast<const f32x4*>(pk);
+    sv += *reinterpret_cast<const f32x4*>(pk + static_cast<size_t>(kKeysPerWg) * D);
+  }
+  const int64_t off = static_cast<int64_t>(key) * Hkv * D + static_cast<int64_t>(kvh) * D + 4 * d4;
+  bf16x4 wk, wv;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    wk[e] = static_cast<__bf16>(sk[e]);
+    wv[e] = static_cast<__bf16>(sv[e]);
+  }
+  *reinterpret_cast<bf16x4*>(dk + off) = wk;
+  *reinterpret_cast<bf16x4*>(dv + off) = wv;
+}
+
+// dscore[c] = sum over KV heads and chunks of part_ds (workgroups below
+// n_ds_blocks, one thread per key); dgain[h] = sum over key blocks, chunks
+// and waves of part_dg (one workgroup per head: strided partial sums, then a
+// tree in LDS).  Fixed order throughout: deterministic.
 __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(const float* __restrict__ part_ds,
                                                               const float* __restrict__ part_dg,
                                                               float* __restrict__ dscore,
                                                               float* __restrict__ dgain,
                                                               int32_t N, int32_t Hq, int32_t Hkv,
-                                                              int32_t n_dg) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < N) {
+                                                              int32_t nkb, int32_t qchunk,
+                                                              int causal, int32_t n_ds_blocks) {
+  const int nq = (N + kTile - 1) / kTile;
+  if (static_cast<int>(blockIdx.x) < n_ds_blocks) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= N) return;
+    const int kb = static_cast<int>(i) / kKeysPerWg, kl = static_cast<int>(i) % kKeysPerWg;
+    const int nc = kv_chunks(kb, nq, qchunk, causal != 0);
     float acc = 0.0f;
-    for (int h = 0; h < Hkv; ++h) acc += part_ds[static_cast<int64_t>(h) * N + i];
+    for (int h = 0; h < Hkv; ++h)
+      for (int c = 0; c < nc; ++c)
+        acc += part_ds[((static_cast<size_t>(c) * nkb + kb) * Hkv + h) * kKeysPerWg + kl];
     dscore[i] = acc;
-  } else if (i < static_cast<int64_t>(N) + Hq) {
-    const int h = static_cast<int>(i - N);
-    float acc = 0.0f;
-    for (int b = 0; b < n_dg; ++b) acc += part_dg[static_cast<int64_t>(b) * Hq + h];
-    dgain[h] = acc;
+    return;
   }
+  const int h = static_cast<int>(blockIdx.x) - n_ds_blocks;
+  const int G = Hq / Hkv, kvh = h / G, hl = h % G;
+  // entries (key block, chunk, wave) in key-block-major order; thread t sums
+  // entries t, t + 256, ...
+  const int per_kb = 4 * ((nq + qchunk - 1) / qchunk);   // upper bound of waves x chunks
+  float acc = 0.0f;
+  for (int e = threadIdx.x; e < nkb * per_kb; e += 256) {
+    const int kb = e / per_kb, c = (e % per_kb) / 4, w = e % 4;
+    if (c < kv_chunks(kb, nq, qchunk, causal != 0)) {
+      const size_t slot = (static_cast<size_t>(c) * nkb + kb) * Hkv + kvh;
+      acc += part_dg[(slot * 4 + w) * G + hl];
+    }
+  }
+  __shared__ float red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int m = 128; m >= 1; m >>= 1) {
+    if (static_cast<int>(threadIdx.x) < m) red[threadIdx.x] += red[threadIdx.x + m];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) dgain[h] = red[0];
 }
 
+// dK/dV query chunks: enough (query chunk, key block, KV head) workgroups to
+// give every CU about three, at most 8 chunks per key block.
 struct BwdWorkspace {
-  size_t delta, lse2, part_ds, part_dg, bytes;   // float offsets, total bytes
+  int32_t nkb, nchunk, qchunk;
+  size_t delta, lse2, part_ds, part_dg, part_kv, bytes;   // float offsets, total bytes
 };
-BwdWorkspace bwd_workspace(int64_t N, int64_t Hq, int64_t Hkv) {
+BwdWorkspace bwd_workspace(int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
   BwdWorkspace w;
-  const int64_t nkb = (N + kKeysPerWg - 1) / kKeysPerWg;
+  w.nkb = static_cast<int32_t>((N + kKeysPerWg - 1) / kKeysPerWg);
+  const int64_t nq = (N + kTile - 1) / kTile;
+  const int64_t pairs = std::max<int64_t>(int64_t{1}, w.nkb * Hkv);
+  const int64_t want = std::min<int64_t>(8, std::max<int64_t>(1, (768 + pairs - 1) / pairs));
+  w.qchunk = static_cast<int32_t>(std::max<int64_t>(1, (nq + want - 1) / want));
+  w.nchunk = static_cast<int32_t>(std::max<int64_t>(1, (nq + w.qchunk - 1) / w.qchunk));
+  const size_t slots = static_cast<size_t>(w.nchunk) * w.nkb * Hkv;
   w.delta = 0;
   w.lse2 = static_cast<size_t>(Hq * N);
   w.part_ds = w.lse2 + static_cast<size_t>(Hq * N);
-  w.part_dg = w.part_ds + static_cast<size_t>(Hkv * N);
-  w.bytes = (w.part_dg + static_cast<size_t>(nkb * 4 * Hq)) * sizeof(float);
+  w.part_dg = w.part_ds + slots * kKeysPerWg;
+  w.part_kv = w.part_dg + slots * 4 * static_cast<size_t>(Hq / Hkv);
+  const size_t kv = w.nchunk > 1 ? slots * 2 * kKeysPerWg * static_cast<size_t>(D) : 0;
+  w.bytes = (w.part_kv + kv) * sizeof(float);
   return w;
 }
 
@@ -620,26 +722,33 @@ template <int D, int HPW, bool CAUSAL, bool B, bool QS>
 void launch_bwd(const BwdArgs& a, const BwdWorkspace& w) {
   constexpr int PB = 32 * (4 / HPW);
   const int32_t npb = (a.N + PB - 1) / PB, nhg = a.Hq / HPW;
-  const int32_t nkb = (a.N + kKeysPerWg - 1) / kKeysPerWg;
+  const int32_t nkb = w.nkb;
   float* delta = a.ws + w.delta;
   float* lse2 = a.ws + w.lse2;
   float* pds = a.ws + w.part_ds;
   float* pdg = a.ws + w.part_dg;
+  float* pkv = a.ws + w.part_kv;
   const int64_t rows = static_cast<int64_t>(a.N) * a.Hq;
   attn_bwd_pre_kernel<D><<<dim3(static_cast<uint32_t>((rows + 255) / 256)), dim3(256), 0, a.s>>>(
       a.out, a.dout, a.lse, delta, lse2, a.N, a.Hq);
-  attn_bwd_dkdv_kernel<D, CAUSAL, B, QS><<<dim3(static_cast<uint32_t>(nkb * a.Hkv)), dim3(256), 0,
-                                           a.s>>>(a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale,
-                                                  a.dout, lse2, delta, a.dk, a.dv, pds, pdg,
-                                                  a.N, a.Hq, a.Hkv);
+  attn_bwd_dkdv_kernel<D, CAUSAL, B, QS>
+      <<<dim3(static_cast<uint32_t>(w.nchunk * nkb * a.Hkv)), dim3(256), 0, a.s>>>(
+          a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.dout, lse2, delta, a.dk, a.dv, pkv, pds,
+          pdg, a.N, a.Hq, a.Hkv, nkb, w.qchunk);
+  if (w.nchunk > 1) {
+    const int64_t n = static_cast<int64_t>(a.N) * a.Hkv * (D / 4);
+    attn_bwd_kv_reduce_kernel<D><<<dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                                   a.s>>>(pkv, a.dk, a.dv, a.N, a.Hkv, nkb, w.qchunk,
+                                          CAUSAL ? 1 : 0);
+  }
   attn_bwd_dq_kernel<D, HPW, CAUSAL, B, QS><<<dim3(static_cast<uint32_t>(npb * nhg)), dim3(256),
                                               0, a.s>>>(a.q, a.k, a.v, a.ks, a.gain, a.qs,
                                                         a.scale, a.dout, lse2, delta, a.dq, a.N,
                                                         a.Hq, a.Hkv, npb, nhg);
   if (B) {
-    const int64_t n = static_cast<int64_t>(a.N) + a.Hq;
-    attn_bwd_reduce_kernel<<<dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, a.s>>>(
-        pds, pdg, a.dscore, a.dgain, a.N, a.Hq, a.Hkv, nkb * 4);
+    const int32_t nds = (a.N + 255) / 256;
+    attn_bwd_reduce_kernel<<<dim3(static_cast<uint32_t>(nds + a.Hq)), dim3(256), 0, a.s>>>(
+        pds, pdg, a.dscore, a.dgain, a.N, a.Hq, a.Hkv, nkb, w.qchunk, CAUSAL ? 1 : 0, nds);
   }
 }
 
@@ -660,10 +769,12 @@ void launch_bwd_d(const BwdArgs& a, const BwdWorkspace& w) {
 }  // namespace
 }  // namespace tg
 
-extern "C" size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv) {
-  if (N < 0 || N > tg::kMaxTokens || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || N * Hq > tg::kMaxTokens)
+extern "C" size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv,
+                                                  int64_t D) {
+  if (N < 0 || N > tg::kMaxTokens || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
+      N * Hq > tg::kMaxTokens || (D != 64 && D != 128))
     return 0;
-  return tg::bwd_workspace(N, Hq, Hkv).bytes;
+  return tg::bwd_workspace(N, Hq, Hkv, D).bytes;
 }
 
 extern "C" tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
@@ -691,7 +802,7 @@ extern "C" tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   if (N * Hq > kMaxTokens || N * Hq * D * 2 > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_bias_attn_bwd: N * Hq * D * 2 must be < 2^31 (32-bit offsets)");
-  const BwdWorkspace w = bwd_workspace(N, Hq, Hkv);
+  const BwdWorkspace w = bwd_workspace(N, Hq, Hkv, D);
   if (w.bytes > 0 && (workspace == nullptr || workspace_bytes < w.bytes))
     return fail(TG_ERR_WORKSPACE, "tg_bias_attn_bwd: workspace of %zu bytes, need %zu",
                 workspace == nullptr ? (size_t)0 : workspace_bytes, w.bytes);

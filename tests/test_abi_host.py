@@ -228,12 +228,17 @@ def _bwd(lib, ws=FAKE, nbytes=1 << 30, dt=BF16, N=64, Hq=4, Hkv=2, D=128, q=FAKE
 
 
 def test_attn_bwd_workspace_size(lib):
-    # Delta and lse2 [Hq][N], dscore partials [Hkv][N], dgain partials
-    # [ceil(N/128) x 4 waves][Hq], all f32
-    assert lib.tg_bias_attn_bwd_workspace_size(2512, 16, 8) == \
-        (2 * 16 * 2512 + 8 * 2512 + 20 * 4 * 16) * 4
-    assert lib.tg_bias_attn_bwd_workspace_size(0, 16, 8) == 0
-    assert lib.tg_bias_attn_bwd_workspace_size(100, 6, 4) == 0   # Hq % Hkv != 0
+    # N = 2512, 16/8 heads, D = 128: 20 key blocks of 128 x 8 KV heads = 160
+    # dK/dV workgroups, split 5 ways (768 / 160 rounded up) into chunks of
+    # 8 of the 40 query tiles: 800 slots.  Delta and lse2 [Hq][N], dscore
+    # partials [slot][128 keys], dgain partials [slot][4 waves][2 heads],
+    # dK and dV partials [slot][2][128][D], all f32
+    slots = 5 * 20 * 8
+    assert lib.tg_bias_attn_bwd_workspace_size(2512, 16, 8, 128) == \
+        (2 * 16 * 2512 + slots * 128 + slots * 4 * 2 + slots * 2 * 128 * 128) * 4
+    assert lib.tg_bias_attn_bwd_workspace_size(0, 16, 8, 128) == 0
+    assert lib.tg_bias_attn_bwd_workspace_size(100, 6, 4, 128) == 0   # Hq % Hkv != 0
+    assert lib.tg_bias_attn_bwd_workspace_size(100, 8, 4, 256) == 0   # head dim 256
 
 
 def test_attn_bwd_validation(lib):
