@@ -56,6 +56,10 @@
 
 #include "tg_common.hpp"
 
+#ifndef TG_ATTN_QW8
+#define TG_ATTN_QW8 1
+#endif
+
 namespace tg {
 namespace {
 
@@ -143,15 +147,18 @@ __host__ __device__ inline int row_tiles(int p, int PB, int N, bool causal) {
   return (end + kBK - 1) / kBK;
 }
 
-template <int D, int HPW, int KS, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE, bool SPLIT>
-__global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_bf16_kernel(
+template <int D, int HPW, int KS, int QW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE,
+          bool SPLIT>
+__global__ __launch_bounds__(64 * QW * KS, (KS == 1 && QW == 4 && D <= 128) ? 2 : 1) void
+attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
     int32_t n_pblocks, int32_t n_hgroups, std::conditional_t<SPLIT, SplitLaunch, NoSplit> sp) {
   static_assert(!SPLIT || KS == 1, "a split chunk runs one key stream");
-  constexpr int PB = 32 * (4 / HPW);        // query positions per workgroup
+  static_assert(QW == 4 || (QW == 8 && KS == 1 && !SPLIT), "8 waves: one key stream, unsplit");
+  constexpr int PB = 32 * (QW / HPW);       // query positions per workgroup
   constexpr int DK = D / 16;                // k-steps of S^T = K Q^T (plus one extra)
   constexpr int DB = D / 32;                // 32-row blocks of O^T
   constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
@@ -164,8 +171,9 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
   // streams' partial softmax states are merged at the end
   __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[2][KS];
 
-  const int tid = threadIdx.x & 255;        // thread index within the key stream
-  const int kh = threadIdx.x >> 8;          // key stream
+  constexpr int NT = 64 * QW;               // threads per key stream
+  const int tid = threadIdx.x % NT;         // thread index within the key stream
+  const int kh = threadIdx.x / NT;          // key stream
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
@@ -187,7 +195,12 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
       const_cast<uint16_t*>(v), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
 
   // ---- staging roles ------------------------------------------------------
-  const int krow = tid / CPR, kchunk = tid % CPR;          // K: row-major copy
+  // 4 waves: every thread stages part of K and part of V.  8 waves (two
+  // query blocks sharing each key tile): threads 0..255 stage V, 256..511 K.
+  const int stid = tid & 255;                              // index within a role
+  const bool k_role = QW == 4 || tid >= 256;
+  const bool v_role = QW == 4 || tid < 256;
+  const int krow = stid / CPR, kchunk = stid % CPR;        // K: row-major copy
   // V: piece tid + 256 pc is keys 4 vkg .. +3 of dims 8 vdc .. +7, with
   // vkg = piece % 16 and vdc = piece / 16
   const float inv_scale = 1.0f / scale;
@@ -204,19 +217,24 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
   auto load_tile = [&](int t) {
     const int k0 = t * kBK;
     const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
+    if (k_role) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i)
-      kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-          k_rs, static_cast<uint32_t>(k0 + krow + KRPI * i) * kv_row + hoff + 16u * kchunk, 0, 0);
+      for (int i = 0; i < KI; ++i)
+        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
+            k_rs, static_cast<uint32_t>(k0 + krow + KRPI * i) * kv_row + hoff + 16u * kchunk, 0,
+            0);
+    }
+    if (v_role) {
 #pragma unroll
-    for (int pc = 0; pc < VPC; ++pc) {
-      const int piece = tid + 256 * pc;
-      const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
-      if (piece < VT) {
+      for (int pc = 0; pc < VPC; ++pc) {
+        const int piece = stid + 256 * pc;
+        const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
+        if (piece < VT) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vreg[pc][j] = __builtin_amdgcn_raw_buffer_load_b128(
-              v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            vreg[pc][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
+        }
       }
     }
     if (HAS_BIAS && tid < HPW * kBK)   // keys past N read 0
@@ -224,12 +242,16 @@ __global__ __launch_bounds__(256 * KS, (KS == 1 && D <= 128) ? 2 : 1) void attn_
                                            s_rs, 4u * static_cast<uint32_t>(k0 + bias_key), 0, 0));
   };
   auto store_tile = [&](AttnSmem<D>& b) {
+    if (k_role) {
 #pragma unroll
-    for (int i = 0; i < KI; ++i)
-      *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) = kreg[i];
+      for (int i = 0; i < KI; ++i)
+        *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) =
+            kreg[i];
+    }
 #pragma unroll
     for (int pc = 0; pc < VPC; ++pc) {
-      const int piece = tid + 256 * pc;
+      if (!v_role) break;
+      const int piece = stid + 256 * pc;
       const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
       if (piece < VT) {
         // keys 4 vkg .. 4 vkg + 3 go to the slots the PV k-step reads them from
@@ -789,10 +811,10 @@ const SplitPlan& split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool 
   return cache.back().plan;
 }
 
-template <int D, int HPW, bool CAUSAL, int KS, bool SPLIT, typename SP>
+template <int D, int HPW, bool CAUSAL, int KS, bool SPLIT, typename SP, int QW = 4>
 void launch_bf16_attn_ks(const AttnArgs& a, dim3 grid, int32_t npb, int32_t nhg, const SP& sp) {
-#define TG_ATTN_LAUNCH(B, Q)                                                                  \
-  attn_bf16_kernel<D, HPW, KS, CAUSAL, B, Q, SPLIT><<<grid, dim3(256 * KS), 0, a.s>>>(       \
+#define TG_ATTN_LAUNCH(B, Q)                                                                 \
+  attn_bf16_kernel<D, HPW, KS, QW, CAUSAL, B, Q, SPLIT><<<grid, dim3(64 * QW * KS), 0, a.s>>>( \
       a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.out, a.lse, a.N, a.Hq, a.Hkv, npb, nhg, sp)
   if (a.has_bias) {
     if (a.has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
@@ -832,6 +854,15 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
       launch_bf16_attn_ks<D, HPW, CAUSAL, 2, false>(a, grid, npb, nhg, none);
       return;
     }
+#if TG_ATTN_QW8
+    // large grids: 8-wave workgroups, two query blocks sharing each staged
+    // key tile (half the staging work per wave at the same occupancy)
+    constexpr int PB8 = 32 * (8 / HPW);
+    const int32_t npb8 = (a.N + PB8 - 1) / PB8;
+    launch_bf16_attn_ks<D, HPW, CAUSAL, 1, false, NoSplit, 8>(
+        a, dim3(static_cast<uint32_t>(static_cast<int64_t>(npb8) * nhg)), npb8, nhg, none);
+    return;
+#endif
   }
   launch_bf16_attn_ks<D, HPW, CAUSAL, 1, false>(a, grid, npb, nhg, none);
 }

@@ -80,6 +80,9 @@ SHAPES = [  # N, Hq, Hkv, D
     (1000, 4, 4, 64),
     # head dim 256 (the pages' second supported head dim)
     (1, 2, 1, 256), (100, 4, 2, 256), (513, 8, 2, 256), (129, 2, 2, 256), (300, 8, 1, 256),
+    # grids of more than 1024 workgroups: the 8-wave launch (two query
+    # blocks per workgroup sharing each key tile)
+    (2100, 64, 64, 64), (4500, 32, 8, 64),
 ]
 
 
