@@ -13,9 +13,10 @@
 //   z[r,c] = c_r * (scale * <q_r, k_c> + gain_h * score_c),   c <= r
 //
 // bf16 path (gfx950, wave64):
-//   * A workgroup (4 waves) owns one KV head and a block of query positions;
-//     each wave owns 32 query positions of one query head, and the HPW query
-//     heads of the group that share the KV head reuse every K/V tile staged
+//   * A workgroup (4 waves, or 8 for large grids) owns one KV head and a
+//     block of query positions; each wave owns 32 query positions of one
+//     query head, and the HPW query heads of the group that share the KV
+//     head (and with 8 waves two query blocks) reuse every K/V tile staged
 //     in LDS.
 //   * Logits are computed transposed, S^T = K Q^T, on
 //     v_mfma_f32_32x32x16_bf16: in the accumulator each lane holds one
@@ -25,12 +26,15 @@
 //     place, are exactly the B operand of the next product O^T += V^T P^T.
 //     The keys that the accumulator layout puts in a lane's k-slots are
 //     matched by reading V^T from LDS in the same order.
-//   * Q stays in registers for the whole key loop.  K tiles are staged in
-//     LDS row-major (padded); V tiles are transposed on their way into LDS
-//     (4 keys x 8 dims per thread, packed with byte permutes), the keys of
-//     every 16-key PV step stored in the order the P^T accumulator holds
-//     them, so each lane's V^T operand is one 16-byte read.  The next tile's
-//     global loads are issued before the current tile's math.
+//   * Q stays in registers for the whole key loop.  K and V tiles go HBM ->
+//     LDS with direct-to-LDS loads (no registers, no LDS write
+//     instructions), row-major with XOR-swizzled 16-byte chunks; the next
+//     tile's loads are issued before the current tile's math and waited for
+//     (vmcnt 0) before the tile barrier.  A lane's V^T operand (8 keys at
+//     one dim) is two transposing LDS reads (ds_read_b64_tr_b16): within a
+//     16-lane group, lane 4a + j reads 4 dims of one key and lane 4a' + b'
+//     receives dim b' of the 4 keys read by lanes a', a' + 4, a' + 8,
+//     a' + 12.
 //   * The two 32-key halves of a tile's logits are independent accumulation
 //     chains, interleaved so no MFMA waits on its own predecessor.
 //   * Key streams: when the grid is small (short prompts, where the longest
@@ -67,26 +71,18 @@ constexpr int kBK = 64;           // keys per tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Slot of the 4-key group g (0..3) of a 16-key PV k-step in V^T: lane half
-// hh reads slots 8hh..8hh+7, which must hold keys 4hh..4hh+3 and 8+4hh..8+4hh+3
-// (the order the P^T accumulator holds them in).
-__device__ __forceinline__ int vgroup_slot(int g) { return ((g & 1) << 1) | (g >> 1); }
-
+// K and V tiles, copied HBM -> LDS by direct-to-LDS loads: row-major
+// [key][D], unpadded, the 16-byte chunk c of key row r stored at chunk
+// c ^ (r & SW), so that the 32 rows a wave reads at one column fall in
+// different banks.  V^T operands are formed at read time by the transposing
+// LDS read.
 template <int D>
 struct AttnSmem {
-  static constexpr int KP = D + 8;          // K row pitch (bf16)
-  static constexpr int VP = kBK + 8;        // V^T row pitch (bf16)
-  uint16_t ks[kBK * KP];                    // K tile, row-major [key][dim]
-  uint16_t vt[D * VP];                      // V tile transposed [dim][key slot]
+  static constexpr int SW = (D / 8 < 16 ? D / 8 : 16) - 1;
+  uint16_t ks[kBK * D];
+  uint16_t vs[kBK * D];
   u32x2 bias[4][kBK];                       // per head: bf16 (hi | mid << 16, lo)
 };
-
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return (a & 0xffffu) | (b << 16);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xffff0000u);
-}
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
@@ -161,15 +157,11 @@ attn_bf16_kernel(
   constexpr int PB = 32 * (QW / HPW);       // query positions per workgroup
   constexpr int DK = D / 16;                // k-steps of S^T = K Q^T (plus one extra)
   constexpr int DB = D / 32;                // 32-row blocks of O^T
-  constexpr int CPR = D / 8;                // 16-byte chunks per K/V row
-  constexpr int KRPI = 256 / CPR;           // K rows staged per pass
-  constexpr int KI = kBK / KRPI;            // K staging passes
-  constexpr int VT = (kBK / 4) * CPR;       // (4 keys x 8 dims) pieces of a V tile
-  constexpr int VPC = (VT + 255) / 256;     // V pieces per staging thread
   // KS key streams: stream kh (waves 4kh .. 4kh+3, threads 256kh ..) takes
   // key tiles kh, kh + KS, kh + 2KS, ... with its own LDS buffers; the
   // streams' partial softmax states are merged at the end
-  __shared__ __attribute__((aligned(16))) AttnSmem<D> sm[2][KS];
+  using Smem = AttnSmem<D>;
+  __shared__ __attribute__((aligned(16))) Smem sm[2][KS];
 
   constexpr int NT = 64 * QW;               // threads per key stream
   const int tid = threadIdx.x % NT;         // thread index within the key stream
@@ -186,93 +178,50 @@ attn_bf16_kernel(
   const int kvh = (hg * HPW) / G;
 
   const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;     // bytes per token
-  const uint32_t kv_row = static_cast<uint32_t>(Hkv) * D * 2;
   const __amdgpu_buffer_rsrc_t q_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(q), 0, static_cast<int>(static_cast<uint32_t>(N) * q_row), 0x00020000);
-  const __amdgpu_buffer_rsrc_t k_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(k), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
-  const __amdgpu_buffer_rsrc_t v_rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(v), 0, static_cast<int>(static_cast<uint32_t>(N) * kv_row), 0x00020000);
 
-  // ---- staging roles ------------------------------------------------------
-  // 4 waves: every thread stages part of K and part of V.  8 waves (two
-  // query blocks sharing each key tile): threads 0..255 stage V, 256..511 K.
-  const int stid = tid & 255;                              // index within a role
-  const bool k_role = QW == 4 || tid >= 256;
-  const bool v_role = QW == 4 || tid < 256;
-  const int krow = stid / CPR, kchunk = stid % CPR;        // K: row-major copy
-  // V: piece tid + 256 pc is keys 4 vkg .. +3 of dims 8 vdc .. +7, with
-  // vkg = piece % 16 and vdc = piece / 16
+  // ---- staging -------------------------------------------------------------
   const float inv_scale = 1.0f / scale;
   // A -inf score becomes a bias of -2^21 log2 units (in dot-product units):
   // for any per-query scale >= 0.25 the logit falls below kMaskedLog2 and its
   // weight underflows to exactly 0, as deleting the key would give.
   const float masked_bias = -2097152.0f * inv_scale / kLog2e;
-  u32x4 kreg[KI], vreg[VPC][4];
   float sreg = 0.0f;        // staged raw score (its bias is formed at store time)
   const int bias_key = tid % kBK;
   const float bias_gain = (HAS_BIAS && tid < HPW * kBK) ? gain[hg * HPW + tid / kBK] : 0.0f;
   const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(key_score), 0, HAS_BIAS ? N * 4 : 0, 0x00020000);
-  auto load_tile = [&](int t) {
+  // each wave of the stream issues its share of the tile's 1-KB pieces; rows
+  // past N re-read row N - 1 (valid memory; those keys are masked)
+  constexpr int PIECES = kBK * D * 2 / 1024;
+  constexpr int PPW = PIECES / QW;
+  static_assert(PPW * QW == PIECES, "whole pieces per wave");
+  auto dma_tile = [&](int t, Smem& b) {
     const int k0 = t * kBK;
-    const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
-    if (k_role) {
 #pragma unroll
-      for (int i = 0; i < KI; ++i)
-        kreg[i] = __builtin_amdgcn_raw_buffer_load_b128(
-            k_rs, static_cast<uint32_t>(k0 + krow + KRPI * i) * kv_row + hoff + 16u * kchunk, 0,
-            0);
-    }
-    if (v_role) {
-#pragma unroll
-      for (int pc = 0; pc < VPC; ++pc) {
-        const int piece = stid + 256 * pc;
-        const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
-        if (piece < VT) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            vreg[pc][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                v_rs, static_cast<uint32_t>(k0 + 4 * vkg + j) * kv_row + hoff + 16u * vdc, 0, 0);
-        }
-      }
+    for (int i = 0; i < PPW; ++i) {
+      const int u = wave * PPW + i;
+      const int byte = u * 1024 + 16 * lane;
+      const int r = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ (r & Smem::SW);
+      const int64_t goff = (static_cast<int64_t>(min(k0 + r, N - 1)) * Hkv + kvh) * D + 8 * c;
+      __builtin_amdgcn_global_load_lds(k + goff, (__attribute__((address_space(3))) void*)&b.ks[u * 512],
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(v + goff, (__attribute__((address_space(3))) void*)&b.vs[u * 512],
+                                       16, 0, 0);
     }
     if (HAS_BIAS && tid < HPW * kBK)   // keys past N read 0
       sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                            s_rs, 4u * static_cast<uint32_t>(k0 + bias_key), 0, 0));
   };
-  auto store_tile = [&](AttnSmem<D>& b) {
-    if (k_role) {
-#pragma unroll
-      for (int i = 0; i < KI; ++i)
-        *reinterpret_cast<u32x4*>(&b.ks[(krow + KRPI * i) * AttnSmem<D>::KP + 8 * kchunk]) =
-            kreg[i];
-    }
-#pragma unroll
-    for (int pc = 0; pc < VPC; ++pc) {
-      if (!v_role) break;
-      const int piece = stid + 256 * pc;
-      const int vkg = piece % (kBK / 4), vdc = piece / (kBK / 4);
-      if (piece < VT) {
-        // keys 4 vkg .. 4 vkg + 3 go to the slots the PV k-step reads them from
-        const int vslot = 16 * (vkg >> 2) + 4 * vgroup_slot(vkg & 3);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          // dims 8 vdc + 2w (low halves) and 8 vdc + 2w + 1 (high halves)
-          u32x2 lo, hi;
-          lo[0] = pack_lo(vreg[pc][0][w], vreg[pc][1][w]);
-          lo[1] = pack_lo(vreg[pc][2][w], vreg[pc][3][w]);
-          hi[0] = pack_hi(vreg[pc][0][w], vreg[pc][1][w]);
-          hi[1] = pack_hi(vreg[pc][2][w], vreg[pc][3][w]);
-          *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w) * AttnSmem<D>::VP + vslot]) = lo;
-          *reinterpret_cast<u32x2*>(&b.vt[(8 * vdc + 2 * w + 1) * AttnSmem<D>::VP + vslot]) = hi;
-        }
-      }
-    }
+  auto store_bias = [&](Smem& b) {
     if (HAS_BIAS && tid < HPW * kBK)
       b.bias[tid / kBK][bias_key] = split_bf16_triple(
           sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale);
   };
+  // vmcnt(0), other counters untouched: every direct-to-LDS load of this
+  // wave has landed (each wave then passes the barrier)
+  auto dma_wait = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   // One item: query block pblock against key tiles [t_first, t_end) of its
   // n_tiles; the final output, or (slot != kNoSlot) the unnormalised state.
@@ -314,18 +263,19 @@ attn_bf16_kernel(
   float l_run = 0.0f;       // this lane's share of the running sum of 2^y
 
   if (t_first + kh < t_end) {
-    load_tile(t_first + kh);
-    store_tile(sm[0][kh]);
+    dma_tile(t_first + kh, sm[0][kh]);
+    store_bias(sm[0][kh]);
   }
+  dma_wait();
   __syncthreads();
 
   const int n_rounds = (t_end - t_first + KS - 1) / KS;
   for (int j = 0; j < n_rounds; ++j) {
     const int t = t_first + KS * j + kh;     // this stream's tile
-    const AttnSmem<D>& b = sm[j & 1][kh];
+    const Smem& b = sm[j & 1][kh];
     const int k0 = t * kBK;
     const bool more = t + KS < t_end;
-    if (more) load_tile(t + KS);
+    if (more) dma_tile(t + KS, sm[(j + 1) & 1][kh]);
     // keep the next tile's loads issued here, ahead of this tile's math
     __builtin_amdgcn_sched_barrier(0);
     if (KS == 1 || t < t_end) {   // uniform per wave: a stream may idle in the last round
@@ -341,8 +291,9 @@ attn_bf16_kernel(
     for (int ks = 0; ks < DK; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
+        const int row = 32 * kb + l32;
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-            &b.ks[(32 * kb + l32) * AttnSmem<D>::KP + 8 * hh + 16 * ks]);
+            &b.ks[row * D + 8 * ((2 * ks + hh) ^ (row & Smem::SW))]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
 #pragma unroll
@@ -416,16 +367,30 @@ attn_bf16_kernel(
       for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const u32x4 a4 = *reinterpret_cast<const u32x4*>(
-              &b.vt[(32 * db + l32) * AttnSmem<D>::VP + 32 * kb + 16 * hf + 8 * hh]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
-                                                          p[kb][hf], o[db], 0, 0, 0);
+          // two transposing reads: within each 16-lane group g, lane 4a + j
+          // reads 4 dims (32 db + 16 (g & 1) + 4a ..) of key
+          // 32 kb + 16 hf + 8 r + 4 (g >> 1) + j, and lane 4a' + b' receives
+          // dim 32 db + 16 (g & 1) + 4a' + b' of the group's keys j = 0..3:
+          // its V^T row, in the key order of the P^T operand
+          const int g = lane >> 4, ja = (lane & 15) >> 2, aa = lane & 3;
+          const int dim = 32 * db + 16 * (g & 1) + 4 * aa;
+          bf16x4 vh[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int key = 32 * kb + 16 * hf + 8 * r + 4 * (g >> 1) + ja;
+            const int off = key * D + 8 * ((dim >> 3) ^ (key & Smem::SW)) + (dim & 7);
+            vh[r] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (__attribute__((address_space(3))) bf16x4*)(const_cast<uint16_t*>(b.vs) + off));
+          }
+          const bf16x8 a8 = __builtin_shufflevector(vh[0], vh[1], 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, p[kb][hf], o[db], 0, 0, 0);
         }
       }
     }
 
     }
-    if (more) store_tile(sm[(j + 1) & 1][kh]);
+    if (more) store_bias(sm[(j + 1) & 1][kh]);
+    dma_wait();
     __syncthreads();
   }
   if (KS > 1) {
