@@ -628,9 +628,9 @@ constexpr int kMinChunkTiles = 4;
 // tile loads) and epilogue; the merge costs a launch plus the chunk states'
 // bytes read back at about 10 MB per unit.
 constexpr double kItemUnits = 1.5;
-// A two-stream workgroup's round of two tiles takes ~1.3 units (its eight
-// waves share every barrier).
-constexpr double kTwoStreamRoundUnits = 1.3;
+// A two-stream workgroup's round of two tiles (one per stream) costs about
+// one unit, as measured with direct-to-LDS staging.
+constexpr double kTwoStreamRoundUnits = 1.0;
 constexpr double kMergeFixedUnits = 1.0;
 constexpr double kMergeBytesPerUnit = 10.0e6;
 // The split must beat the unsplit launch by this factor to be used.

@@ -186,20 +186,20 @@ def test_attn_validation(lib):
 
 def _attn_ws(lib, ws, nbytes, dt=BF16, N=2512, Hq=16, Hkv=8, D=128, q=FAKE, out=FAKE):
     return lib.tg_bias_attn_fwd_ws(dt, N, Hq, Hkv, D, q, FAKE, FAKE, FAKE, FAKE, None,
-                                   ctypes.c_float(0.0), 1, out, None, ws, nbytes, None)
+                                   ctypes.c_float(0.0), 0, out, None, ws, nbytes, None)
 
 
 def test_attn_workspace_size(lib):
     size = lambda *a: lib.tg_bias_attn_workspace_size(*a)
-    # N = 2512, 16/8 heads, D = 128, causal: 40 rows of 64 queries (row p has
-    # p + 1 key tiles) x 8 head groups; the plan cuts rows into chunks of 15
-    # tiles, so rows 15..39 (25 rows) are split, each with state slots for 3
-    # chunks per head group: 25 x 3 x 8 slots of 4 waves x (4 x 16 x 64 + 128)
-    # floats
-    assert size(BF16, 2512, 16, 8, 128, 1) == 25 * 3 * 8 * 4 * (4 * 16 * 64 + 128) * 4
+    # N = 2512, 8/2 heads, D = 256, causal: 4 query heads per KV head, so 79
+    # rows of 32 queries (row p has ceil(32 (p + 1) / 64) key tiles) x 2 head
+    # groups; the plan cuts rows into chunks of 15 tiles, so rows 30..78 (49
+    # rows) are split, with state slots for 3 chunks per head group: 49 x 3 x
+    # 2 slots of 4 waves x (8 x 16 x 64 + 128) floats
+    assert size(BF16, 2512, 8, 2, 256, 1) == 49 * 3 * 2 * 4 * (8 * 16 * 64 + 128) * 4
+    # the same prompt at 16/8 heads, D = 128: two key streams beat the split
+    assert size(BF16, 2512, 16, 8, 128, 1) == 0
     assert size(F32, 2512, 16, 8, 128, 1) == 0          # fp32 path never splits
-    d256 = size(BF16, 2512, 8, 2, 256, 1)                # head dim 256 splits too
-    assert d256 > 0 and d256 % (4 * (8 * 16 * 64 + 128) * 4) == 0
     assert size(BF16, 32768, 16, 8, 128, 1) == 0        # grid fills the chip
     assert size(BF16, 100, 16, 8, 128, 1) == 0          # rows too short to cut
     assert size(BF16, 0, 16, 8, 128, 1) == 0
@@ -209,7 +209,7 @@ def test_attn_workspace_size(lib):
 
 
 def test_attn_ws_validation(lib):
-    need = lib.tg_bias_attn_workspace_size(BF16, 2512, 16, 8, 128, 1)
+    need = lib.tg_bias_attn_workspace_size(BF16, 2512, 16, 8, 128, 0)   # non-causal splits
     assert _attn_ws(lib, FAKE, 0) == WS
     assert b"workspace" in lib.tg_last_error()
     assert _attn_ws(lib, FAKE, need - 1) == WS

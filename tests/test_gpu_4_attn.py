@@ -219,10 +219,10 @@ def test_attn_bf16_dense_sampled_rows():
 
 # ---- split-key path (tg_bias_attn_fwd_ws) ---------------------------------------
 SPLIT_SHAPES = [  # N, Hq, Hkv, D, causal: each takes the split (3 to 7 chunks per long row)
-    (1000, 16, 2, 128, True), (1000, 16, 2, 128, False),   # 4 heads per KV head
+    (1000, 16, 2, 128, True), (2000, 8, 8, 128, False),    # 4 and 1 heads per KV head
     (1000, 4, 4, 64, True), (1000, 4, 4, 64, False),       # 1 head per KV head
     (1700, 6, 2, 64, True), (1700, 6, 2, 64, False),       # 3 heads per KV head
-    (2512, 16, 8, 128, True), (2512, 16, 8, 128, False),   # the 16k prompt's kept set
+    (2512, 8, 4, 128, True), (2512, 16, 8, 128, False),    # the 16k prompt's kept set size
     (1500, 16, 8, 128, True),
     (1800, 12, 4, 64, True),
     (2999, 8, 8, 128, True),                               # ragged last query block
@@ -252,7 +252,7 @@ def test_attn_split_masked_chunks():
     them; rows 0..1599 see no key at all (O = 0, lse = -inf)."""
     rng = np.random.default_rng(86)
     N = 2512
-    q, k, v, s, g, c = make(rng, N, 16, 8, 128, "bf16")
+    q, k, v, s, g, c = make(rng, N, 8, 4, 128, "bf16")
     s[:1600] = -np.inf
     o, lse = gpu_split(q, k, v, s, g, c)
     assert torch.all(o[:1600].float() == 0)
@@ -264,7 +264,7 @@ def test_attn_split_masked_chunks():
 
 def test_attn_split_all_masked():
     rng = np.random.default_rng(87)
-    q, k, v, s, g, c = make(rng, 2512, 16, 8, 128, "bf16")
+    q, k, v, s, g, c = make(rng, 2512, 8, 4, 128, "bf16")
     s[:] = -np.inf
     o, lse = gpu_split(q, k, v, s, g, c)
     assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
@@ -272,7 +272,7 @@ def test_attn_split_all_masked():
 
 def test_attn_split_matches_unsplit_and_is_deterministic():
     rng = np.random.default_rng(88)
-    q, k, v, s, g, c = make(rng, 2512, 16, 8, 128, "bf16")
+    q, k, v, s, g, c = make(rng, 2512, 8, 4, 128, "bf16")
     o1, l1 = gpu_split(q, k, v, s, g, c)
     o2, l2 = gpu_split(q, k, v, s, g, c)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
@@ -296,8 +296,9 @@ def test_attn_split_workspace_unused_shape_runs_unsplit():
 
 
 def test_attn_bf16_t16k_full_split():
-    """The 16k prompt's kept set through the split path: every output row."""
-    w = workloads.get("t16k")
+    """The 16k prompt's kept set at head dim 256 (8/2 heads) through the
+    split path: every output row."""
+    w = workloads.get("t16k-d256")
     _, a = workloads.generate(w)
     rng = np.random.default_rng(92)
     s = rng.standard_normal(w.n_kept).astype(np.float32)

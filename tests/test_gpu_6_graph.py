@@ -103,7 +103,7 @@ CASES = [
     ("t16k", True, 0, False),
     ("t16k", False, 0, False),
     ("t16k", True, 2, False),    # with the lower layers' KV gather on a forked stream
-    ("t16k", True, 2, True),     # and the split-key attention with its workspace
+    ("t16k-d256", True, 2, True),   # head dim 256: the split-key attention and its workspace
     ("multi", True, 0, False),   # T > 32768: the multi-workgroup top-K and its workspace
 ]
 
