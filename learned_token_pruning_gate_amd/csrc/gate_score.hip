@@ -459,24 +459,37 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   const int ss_tile = NW == 8 ? (wave & 3) : wave;
   const int ss_half = NW == 8 ? (wave >> 2) : 0;
 
-  auto stage = [&](int s, const XSlot& sl, const u32x4 (&wc)[NTW][2], XSlot& nsl,
-                   u32x4 (&wn)[NTW][2]) {
-    const int last = nstages - 1;
-    wait_own(s + DEPTH - 1 <= last ? DEPTH - 1 : last - s);
-    // every wave's stage s has landed; every wave is done reading stage s-1
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-    __builtin_amdgcn_s_barrier();
-    u32x4 av[2][4];
+  // One stage ahead: stage s's A fragments (and this wave's sum-of-squares
+  // fragment) sit in registers, read during stage s-1, so the LDS latency of
+  // a stage's reads and the barrier before them overlap the previous stage's
+  // MFMAs instead of preceding this stage's.
+  u32x4 av[2][4];
+  u32x4 mine[2];   // XPW of them
+  auto read_frags = [&](const XSlot& sl, u32x4 (&a)[2][4], u32x4 (&mn)[2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) av[kk][m] = sl.b[m * 2 + kk][lane];
-    u32x4 mine[2];   // this wave's sum-of-squares fragments (XPW of them)
+      for (int m = 0; m < 4; ++m) a[kk][m] = sl.b[m * 2 + kk][lane];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      if (i < XPW) mine[i] = sl.b[ss_tile * 2 + (NW == 8 ? ss_half : i)][lane];
+      if (i < XPW) mn[i] = sl.b[ss_tile * 2 + (NW == 8 ? ss_half : i)][lane];
+  };
+  auto stage = [&](int s, const XSlot& sl_next, const u32x4 (&wc)[NTW][2], XSlot& nsl,
+                   u32x4 (&wn)[NTW][2]) {
+    const int last = nstages - 1;
+    u32x4 an[2][4];
+    u32x4 mn[2];
+    if (s < last) {
+      // this wave's loads of stage s+1 are done (later stages may still be in
+      // flight) and its reads of stage s have returned; after the barrier
+      // every wave's stage s+1 has landed, and stage s-1's slot is free
+      wait_own(s + DEPTH - 1 <= last ? DEPTH - 2 : last - s - 1);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+      read_frags(sl_next, an, mn);
+    }
     if (s + DEPTH <= last) issue(s + DEPTH, nsl, wn);
-    // keep the prefetch issued here, ahead of this stage's MFMAs
+    // keep the reads and the prefetch issued here, ahead of this stage's MFMAs
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -494,12 +507,24 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
               __builtin_bit_cast(bf16x8, av[kk][m]), __builtin_bit_cast(bf16x8, wc[nt][kk]),
               acc[m][nt], 0, 0, 0);
     }
+    // every MFMA of this stage is issued before the next stage's barrier: a
+    // wave waiting there has its matrix work queued behind it
+    __builtin_amdgcn_sched_barrier(0);
+    if (s < last) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) av[kk][m] = an[kk][m];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) mine[i] = mn[i];
+    }
   };
   // slot j of the ring: LDS object xs<j>, register set wr[j]
-#define TG_STAGE_SLOT(S, J)                                                        \
-  stage((S), xs##J, wr[J], (J + DEPTH) % R == 0 ? xs0 : (J + DEPTH) % R == 1 ? xs1 \
-        : (J + DEPTH) % R == 2 ? xs2 : (J + DEPTH) % R == 3 ? xs3 : (J + DEPTH) % R == 4 ? xs4 \
-        : (J + DEPTH) % R == 5 ? xs5 : (J + DEPTH) % R == 6 ? xs6 : xs7, wr[(J + DEPTH) % R])
+#define TG_SLOT(X)                                                                  \
+  ((X) == 0 ? xs0 : (X) == 1 ? xs1 : (X) == 2 ? xs2 : (X) == 3 ? xs3 : (X) == 4 ? xs4 \
+   : (X) == 5 ? xs5 : (X) == 6 ? xs6 : xs7)
+#define TG_STAGE_SLOT(S, J) \
+  stage((S), TG_SLOT((J + 1) % R), wr[J], TG_SLOT((J + DEPTH) % R), wr[(J + DEPTH) % R])
   auto run = [&](int s, int j) {   // j == s % R, a constant after unrolling
     switch (j) {
       case 0: TG_STAGE_SLOT(s, 0); break;
@@ -513,7 +538,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     }
   };
 #undef TG_STAGE_SLOT
-  // prologue: stages 0 .. DEPTH-1 in flight (nstages >= 2; later ones guarded)
+#undef TG_SLOT
+  // prologue: stages 0 .. DEPTH-1 in flight (nstages >= 2; later ones guarded),
+  // then stage 0's fragments into registers
   issue(0, xs0, wr[0]);
   issue(1, xs1, wr[1]);
   if constexpr (DEPTH > 2) if (2 < nstages) issue(2, xs2, wr[2 % R]);
@@ -521,6 +548,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   if constexpr (DEPTH > 4) if (4 < nstages) issue(4, xs4, wr[4 % R]);
   if constexpr (DEPTH > 5) if (5 < nstages) issue(5, xs5, wr[5 % R]);
   if constexpr (DEPTH > 6) if (6 < nstages) issue(6, xs6, wr[6 % R]);
+  wait_own(nstages - 1 < DEPTH - 1 ? nstages - 1 : DEPTH - 1);
+  __builtin_amdgcn_s_barrier();
+  read_frags(xs0, av, mine);
   if constexpr (NST > 0) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) run(s, s % R);
