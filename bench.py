@@ -86,36 +86,50 @@ def cpu_baseline(w, g, a, N, kept, scores_gpu, key_score):
 
     T = w.T
     pr = np.nonzero(g.prunable)[0]
-    n_gate = min(1024, len(pr))
+    # gate: every prunable row up to 16384 of them (spread evenly beyond)
+    n_gate = min(16384, len(pr))
     gate_rows = pr[np.linspace(0, len(pr) - 1, n_gate).astype(np.int64)]
     t0 = time.perf_counter()
     oracle.gate_score(workloads.as_f64(g.resid[gate_rows], w.dtype), g.prunable[gate_rows],
                       workloads.as_f64(g.w1, w.dtype), g.w2, b2=g.b2, gamma=g.gamma, b1=g.b1,
                       eps=g.eps)
-    t_gate = (time.perf_counter() - t0) * len(pr) / n_gate
+    t_gate_sample = time.perf_counter() - t0
+    t_gate = t_gate_sample * len(pr) / n_gate
     t0 = time.perf_counter()
     oracle.topk_select(scores_gpu, g.prunable, w.K)
     t_sel = time.perf_counter() - t0
     t0 = time.perf_counter()
     oracle.compact_gather(g.resid, scores_gpu, kept)
     t_gat = time.perf_counter() - t0
-    n_rows = min(64, N)
-    rows = np.linspace(0, N - 1, n_rows).astype(np.int64)
-    t0 = time.perf_counter()
-    oracle.bias_attn(workloads.as_f64(a.q, w.dtype), workloads.as_f64(a.k, w.dtype),
-                     workloads.as_f64(a.v, w.dtype), key_score, a.gain, rows=rows)
-    t_att_sample = time.perf_counter() - t0
+    # attention: query rows spread over [0, N); a 64-row probe sets how many
+    # rows fill about one second, capped at N (every row)
+    q64, k64, v64 = (workloads.as_f64(x, w.dtype) for x in (a.q, a.k, a.v))
+
+    def attn_rows(n):
+        rows = np.unique(np.linspace(0, N - 1, n).astype(np.int64))
+        t0 = time.perf_counter()
+        oracle.bias_attn(q64, k64, v64, key_score, a.gain, rows=rows)
+        return rows, time.perf_counter() - t0
+
+    rows, t_att_sample = attn_rows(min(64, N))
+    per_work = t_att_sample / float(np.sum(rows + 1))
+    want = int(1.0 / max(per_work, 1e-12) / max(1.0, (N + 1) / 2.0))
+    if want > len(rows):
+        rows, t_att_sample = attn_rows(min(N, want))
+    n_rows = len(rows)
     # causal work of row r is proportional to r + 1
     t_att = t_att_sample * (N * (N + 1) / 2) / float(np.sum(rows + 1))
     total = t_gate + t_sel + t_gat + t_att
-    sample_s = t_gate * n_gate / len(pr) + t_sel + t_gat + t_att_sample
+    sample_s = t_gate_sample + t_sel + t_gat + t_att_sample
+    threads = oracle.num_threads()
     return {
-        "value": T / total, "unit": "tokens/s", "cores": oracle.num_threads(),
+        "value": T / total, "unit": "tokens/s", "cores": threads,
         "kind": "oracle",
         "sample": ("fp64 C oracle on this host: gate on %d of %d prunable rows, full top-K "
                    "and gather, attention on %d of %d query rows (all heads); each stage "
                    "scaled to the full step by its row count (attention by causal work); "
-                   "%.1f s of CPU work" % (n_gate, len(pr), n_rows, N, sample_s)),
+                   "%.1f s wall on %d threads (about %.0f s of CPU work)"
+                   % (n_gate, len(pr), n_rows, N, sample_s, threads, sample_s * threads)),
         "stage_seconds_est": {"gate": t_gate, "select": t_sel, "gather": t_gat,
                               "attn": t_att},
     }
