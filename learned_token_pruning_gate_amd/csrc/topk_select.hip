@@ -458,17 +458,33 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
       for (uint32_t b = tid; b < nb; b += kOneThreads) hist[b] = 0;
       __syncthreads();
     }
-    for (int t = tid; t < T; t += kOneThreads) {
-      const uint32_t k = keys[t];
-      if (k != 0 && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+    // thread tid takes keys 4 tid + 4096 i .. + 3 with 16-byte LDS reads
+    // (staged keys past T, up to the next multiple of 16, are 0: skipped)
+#pragma unroll
+    for (int i = 0; i < kLdsTokens / (4 * kOneThreads); ++i) {
+      const int t = 4 * tid + 4 * kOneThreads * i;
+      if (t < T) {
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[t]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t k = kv[e];
+          if (k != 0 && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+        }
+      }
     }
     __syncthreads();
     if (tid < 64) {
-      // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys)
+      // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys),
+      // kept in registers for the search below
       const int bpl = static_cast<int>(nb) / 64;
       const int top = static_cast<int>(nb) - 1 - lane * bpl;
+      uint32_t cnt[32];
       uint32_t mine = 0;
-      for (int j = 0; j < bpl; ++j) mine += hist[top - j];
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        cnt[j] = j < bpl ? hist[top - j] : 0u;
+        mine += cnt[j];
+      }
       const uint32_t incl = wave_inclusive_scan(mine);
       const uint32_t total = __shfl(incl, 63, 64);
       uint32_t nd = need;
@@ -485,16 +501,16 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
       }
       const uint32_t above = incl - mine;
       if (nd != 0 && above < nd && nd <= above + mine) {
+        // the one bin where the running count first reaches nd
         uint32_t cum = above;
-        for (int j = 0; j < bpl; ++j) {
-          const int b = top - j;
-          const uint32_t c = hist[b];
-          if (cum + c >= nd) {
-            s_state[0] = prefix | (static_cast<uint32_t>(b) << shift);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const uint32_t c = cnt[j];
+          if (cum < nd && cum + c >= nd) {
+            s_state[0] = prefix | (static_cast<uint32_t>(top - j) << shift);
             s_state[1] = mask | ((nb - 1) << shift);
             s_state[2] = nd - cum;
             s_state[3] = (nd - cum == c || pass == 2) ? 1u : 0u;
-            break;
           }
           cum += c;
         }
