@@ -400,18 +400,30 @@ __device__ __forceinline__ void wg_inclusive_scan2(uint32_t& a, uint32_t& b, uin
   tot_b = tb;
 }
 
+// MAXT: the most tokens the launch may stage.  At MAXT <= 16384 the keys
+// leave room for NCOPY copies of the first digit's histogram, bin-major (the
+// copies of a bin in adjacent banks), lane l adding to copy l % NCOPY: the
+// first digit (sign, exponent and two mantissa bits) puts most scores in a
+// few bins, and the copies cut the same-address conflicts of the LDS atomics.
+template <int MAXT>
 __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
     uint32_t K, int32_t* __restrict__ kept_idx, int64_t capacity,
     int32_t* __restrict__ n_kept) {
-  __shared__ __attribute__((aligned(16))) uint32_t keys[kLdsTokens];
+  constexpr int NCOPY = MAXT <= 16384 ? 8 : 1;
+  __shared__ __attribute__((aligned(16))) uint32_t keys[MAXT];
   __shared__ uint32_t hist[2048];
+  __shared__ __attribute__((aligned(16))) uint32_t histc[NCOPY > 1 ? 2048 * NCOPY : 4];
   __shared__ uint32_t s_wave[2 * (kOneThreads / 64)];
   __shared__ uint32_t s_state[4];   // prefix, mask, need, resolved
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
   for (int b = tid; b < 2048; b += kOneThreads) hist[b] = 0;
+  if constexpr (NCOPY > 1)
+#pragma unroll
+    for (int b = 4 * tid; b < 2048 * NCOPY; b += 4 * kOneThreads)
+      *reinterpret_cast<u32x4*>(&histc[b]) = u32x4{0, 0, 0, 0};
   // staging: each thread takes 16 consecutive tokens per round with 16-byte
   // buffer loads (all issued before any is used); past T they read zeros,
   // i.e. non-prunable (the thread holding the tail reads its bytes singly)
@@ -440,7 +452,7 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
           const bool p = ((pm[j] >> (8 * e)) & 0xffu) != 0;
           kv[e] = p ? score_key(__uint_as_float(sv[j][e])) + 1u : 0u;
         }
-        // t0 + 15 < kLdsTokens: t0 is a multiple of 16 below T <= kLdsTokens
+        // t0 + 15 < MAXT: t0 is a multiple of 16 below T <= MAXT
         *reinterpret_cast<u32x4*>(&keys[t0 + 4 * j]) = kv;
       }
     }
@@ -461,18 +473,36 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     // thread tid takes keys 4 tid + 4096 i .. + 3 with 16-byte LDS reads
     // (staged keys past T, up to the next multiple of 16, are 0: skipped)
 #pragma unroll
-    for (int i = 0; i < kLdsTokens / (4 * kOneThreads); ++i) {
+    for (int i = 0; i < MAXT / (4 * kOneThreads); ++i) {
       const int t = 4 * tid + 4 * kOneThreads * i;
       if (t < T) {
         const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[t]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const uint32_t k = kv[e];
-          if (k != 0 && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & (nb - 1)], 1u);
+          if (k != 0 && (k & mask) == prefix) {
+            const uint32_t bin = (k >> shift) & (nb - 1);
+            if (NCOPY > 1 && pass == 0)
+              atomicAdd(&histc[bin * NCOPY + (lane & (NCOPY - 1))], 1u);
+            else
+              atomicAdd(&hist[bin], 1u);
+          }
         }
       }
     }
     __syncthreads();
+    if (NCOPY > 1 && pass == 0) {   // fold the copies into hist
+      for (int b = tid; b < 2048; b += kOneThreads) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int j = 0; j < NCOPY; j += 4) {
+          const u32x4 v4 = *reinterpret_cast<const u32x4*>(&histc[b * NCOPY + j]);
+          c += v4[0] + v4[1] + v4[2] + v4[3];
+        }
+        hist[b] = c;
+      }
+      __syncthreads();
+    }
     if (tid < 64) {
       // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys),
       // kept in registers for the search below
@@ -616,9 +646,12 @@ extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_
 
   const uint32_t Kc = static_cast<uint32_t>(K < T ? K : T);
   if (T <= kLdsTokens && aligned(prunable, 16)) {
-    select_one_wg_kernel<<<dim3(1), dim3(kOneThreads), 0, s>>>(scores, prunable,
-                                                               static_cast<int32_t>(T), Kc,
-                                                               kept_idx, kept_capacity, n_kept);
+    if (T <= kLdsTokens / 2)
+      select_one_wg_kernel<kLdsTokens / 2><<<dim3(1), dim3(kOneThreads), 0, s>>>(
+          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept);
+    else
+      select_one_wg_kernel<kLdsTokens><<<dim3(1), dim3(kOneThreads), 0, s>>>(
+          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept);
     return check_launch("tg_topk_select");
   }
   int64_t per_block = 0;
