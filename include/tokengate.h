@@ -206,7 +206,9 @@ tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
  *   kv = h / (Hq / Hkv)
  *   z  = q_scale[r] * ( softmax_scale * <Q[r,h,:], K[c,kv,:]> + gain[h] * key_score[c] )
  *   O[r,h,:] = sum_c softmax_c(z) * V[c,kv,:],   lse[h][r] = log sum_c exp(z)
- * A row whose logits are all -inf gets O = 0 and lse = -inf.
+ * A row whose logits are all -inf gets O = 0 and lse = -inf.  Inputs are
+ * finite, except key_score, which may be -inf (the key is deleted); a NaN
+ * anywhere gives unspecified results (the kernels are built assuming none).
  *
  * dt            TG_DTYPE_BF16 (bf16 MFMA, fp32 softmax) or TG_DTYPE_F32.
  * N             kept tokens, 0 <= N <= 2^31 - 1 (N == 0 is a no-op).

@@ -29,6 +29,14 @@ CFLAGS = ["-x", "hip", "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
           "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-source flags.  The attention is compiled with IEEE mode off and NaN
+# handling relaxed (infinities are still honoured): its logits come from
+# MFMA products and its masks use -inf, never NaN, and without IEEE mode the
+# running max needs no canonicalising instruction per logit (v_max3 forms
+# directly), which measured 3-5% faster with bit-identical output.
+FILE_FLAGS = {"bias_attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def hipcc() -> str:
     for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if c and os.path.exists(c):
@@ -38,7 +46,8 @@ def hipcc() -> str:
 
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + CFLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + CFLAGS + FILE_FLAGS.get(src, []) + list(extra) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     p = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (p.stdout + p.stderr).splitlines()
             if "packed-fp32-ops' is not a recognized feature" not in l]
