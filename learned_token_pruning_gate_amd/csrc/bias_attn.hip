@@ -283,12 +283,14 @@ attn_bf16_kernel(
   __syncthreads();
 
   const int n_rounds = (t_end - t_first + KS - 1) / KS;
-  for (int j = 0; j < n_rounds; ++j) {
+  // one round; b is this round's buffer and nb the next one's.  Called with
+  // fixed buffers for even and odd rounds, so every LDS address of a round is
+  // a loop-invariant register plus an immediate.
+  auto round = [&](const int j, const Smem& b, Smem& nb) __attribute__((always_inline)) {
     const int t = t_first + KS * j + kh;     // this stream's tile
-    const Smem& b = sm[j & 1][kh];
     const int k0 = t * kBK;
     const bool more = t + KS < t_end;
-    if (more) dma_tile(t + KS, sm[(j + 1) & 1][kh]);
+    if (more) dma_tile(t + KS, nb);
     // keep the next tile's loads issued here, ahead of this tile's math
     __builtin_amdgcn_sched_barrier(0);
     if (KS == 1 || t < t_end) {   // uniform per wave: a stream may idle in the last round
@@ -401,10 +403,16 @@ attn_bf16_kernel(
     }
 
     }
-    if (more) store_bias(sm[(j + 1) & 1][kh]);
+    if (more) store_bias(nb);
     dma_wait();
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < n_rounds; j += 2) {
+    round(j, sm[0][kh], sm[1][kh]);
+    round(j + 1, sm[1][kh], sm[0][kh]);
   }
+  if (j < n_rounds) round(j, sm[0][kh], sm[1][kh]);
   if (KS > 1) {
     // merge the streams' (running max, partial sums, O^T) into stream 0
     constexpr int NV = DB * 16 + 2;
