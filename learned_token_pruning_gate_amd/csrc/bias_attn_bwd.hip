@@ -211,7 +211,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const int hw = wave % HPW;
   const int head = hg * HPW + hw;
   const int kvh = (hg * HPW) / G;
-  const int my_q = pblock * PB + 32 * (wave / HPW) + l32;
+  const int pos0 = pblock * PB + 32 * (wave / HPW);   // the wave's first query
+  const int my_q = pos0 + l32;
   const bool q_ok = my_q < N;
 
   const uint32_t q_row = static_cast<uint32_t>(Hq) * D * 2;
@@ -227,6 +228,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const float zs = scale * cr;            // dZ' = dZ c alpha
   const float l2q = q_ok ? lse2[static_cast<int64_t>(head) * N + my_q] : INFINITY;
   const float dlq = q_ok ? delta[static_cast<int64_t>(head) * N + my_q] : 0.0f;
+  // P zs = 2^(y - lse2 + log2 zs): the factor zs rides in the exponent
+  const float l2z = l2q - __builtin_log2f(zs);
 
   bf16x8 qf[DK + 1], df[DK];
   {
@@ -312,20 +315,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ke), qf[DK],
                                                       s[kb], 0, 0, 0);
     }
-    // weights, masked where the key is past the query or past N
+    // weights, masked where the key is past the query or past N; a tile
+    // whose last key (k0 + 63) no lane of the wave passes needs no mask
     const int rel = lim - k0 - 4 * hh;   // key k0 + 4hh + c visible iff c <= rel
+    const bool full = k0 + kTile - 1 <= (CAUSAL ? min(pos0, N - 1) : N - 1);   // wave-uniform
     bf16x8 zb[2][2];
+    auto weights = [&](const bool masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+        for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * hf + i;
-          const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
-          const float p = c <= rel ? __builtin_amdgcn_exp2f(fmaf(s[kb][r], ac, -l2q)) : 0.0f;
-          zb[kb][hf][i] = static_cast<__bf16>(p * (dp[kb][r] - dlq) * zs);
-        }
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * hf + i;
+            const int c = 32 * kb + 8 * (r >> 2) + (r & 3);
+            const float pz = __builtin_amdgcn_exp2f(fmaf(s[kb][r], ac, -l2z));   // P zs
+            zb[kb][hf][i] = static_cast<__bf16>((masked && c > rel) ? 0.0f : pz * (dp[kb][r] - dlq));
+          }
+    };
+    if (full) weights(false); else weights(true);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -366,7 +374,7 @@ template <int D>
 struct DkvSmem {
   RowTile<D> q, d;
   TrTile<D> qt, dt;
-  float ac[kTile], l2[kTile], dl[kTile];
+  float ac[kTile], acl[kTile], l2[kTile], dl[kTile];   // acl = ac ln 2
 };
 
 template <int D, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
@@ -454,6 +462,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     St::store_pieces(b.dt, dpc, tid);
     if (tid < kTile) {
       b.ac[tid] = vec_ac;
+      b.acl[tid] = vec_ac * kLn2;
       b.l2[tid] = vec_l2;
       b.dl[tid] = vec_dl;
     }
@@ -510,27 +519,35 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     for (int qb = 0; qb < 2; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, kf[DK], s[qb], 0, 0, 0);
 
-    // element (qb, r) is query q0 + 32 qb + 8 (r / 4) + 4 hh + r % 4 and key my_k
+    // element (qb, r) is query q0 + 32 qb + 8 (r / 4) + 4 hh + r % 4 and key
+    // my_k; a tile that every key of the wave sees whole needs no mask
+    const bool full = (!CAUSAL || q0 >= key0 + 32 * wave + 31) &&
+                      key0 + 32 * wave + 32 <= N;   // wave-uniform
     bf16x8 pb[2][2], zb[2][2];
+    auto weights = [&](const bool masked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qi = 32 * qb + 8 * j + 4 * hh;
-        const f32x4 vac = *reinterpret_cast<const f32x4*>(&b.ac[qi]);
-        const f32x4 vl2 = *reinterpret_cast<const f32x4*>(&b.l2[qi]);
-        const f32x4 vdl = *reinterpret_cast<const f32x4*>(&b.dl[qi]);
+        for (int j = 0; j < 4; ++j) {
+          const int qi = 32 * qb + 8 * j + 4 * hh;
+          const f32x4 vac = *reinterpret_cast<const f32x4*>(&b.ac[qi]);
+          const f32x4 vacl = *reinterpret_cast<const f32x4*>(&b.acl[qi]);
+          const f32x4 vl2 = *reinterpret_cast<const f32x4*>(&b.l2[qi]);
+          const f32x4 vdl = *reinterpret_cast<const f32x4*>(&b.dl[qi]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const bool vis = k_ok && (!CAUSAL || my_k <= q0 + qi + i);
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[qb][r], vac[i], -vl2[i])) : 0.0f;
-          const float dz = p * (dp[qb][r] - vdl[i]);
-          a_sum = fmaf(vac[i], dz, a_sum);
-          pb[qb][r >> 3][r & 7] = static_cast<__bf16>(p);
-          zb[qb][r >> 3][r & 7] = static_cast<__bf16>(dz * vac[i] * kLn2);   // dZ c alpha
+          for (int i = 0; i < 4; ++i) {
+            const int r = 4 * j + i;
+            const bool vis = !masked || (k_ok && (!CAUSAL || my_k <= q0 + qi + i));
+            const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][r], vac[i], -vl2[i]));
+            const float p = vis ? e : 0.0f;
+            const float dz = p * (dp[qb][r] - vdl[i]);
+            a_sum = fmaf(vac[i], dz, a_sum);
+            pb[qb][r >> 3][r & 7] = static_cast<__bf16>(p);
+            zb[qb][r >> 3][r & 7] = static_cast<__bf16>(dz * vacl[i]);   // dZ c alpha
+          }
         }
-      }
+    };
+    if (full) weights(false); else weights(true);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
