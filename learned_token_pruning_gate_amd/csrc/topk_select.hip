@@ -412,14 +412,16 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     int32_t* __restrict__ n_kept) {
   constexpr int NCOPY = MAXT <= 16384 ? 8 : 1;
   __shared__ __attribute__((aligned(16))) uint32_t keys[MAXT];
-  __shared__ uint32_t hist[2048];
+  // the digit histograms and the resolved state, double-buffered by pass:
+  // the next pass's histogram is cleared while wave 0 scans this one's
+  __shared__ uint32_t hist2[2][2048];
   __shared__ __attribute__((aligned(16))) uint32_t histc[NCOPY > 1 ? 2048 * NCOPY : 4];
   __shared__ uint32_t s_wave[2 * (kOneThreads / 64)];
-  __shared__ uint32_t s_state[4];   // prefix, mask, need, resolved
+  __shared__ uint32_t s_state2[2][4];   // prefix, mask, need, resolved
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
-  for (int b = tid; b < 2048; b += kOneThreads) hist[b] = 0;
+  for (int b = tid; b < 2048; b += kOneThreads) hist2[0][b] = 0;
   if constexpr (NCOPY > 1)
 #pragma unroll
     for (int b = 4 * tid; b < 2048 * NCOPY; b += 4 * kOneThreads)
@@ -466,10 +468,8 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     const int bits = pass == 2 ? 10 : 11;
     const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
     const uint32_t nb = 1u << bits;
-    if (pass > 0) {
-      for (uint32_t b = tid; b < nb; b += kOneThreads) hist[b] = 0;
-      __syncthreads();
-    }
+    uint32_t* hist = hist2[pass & 1];
+    uint32_t* s_state = s_state2[pass & 1];
     // thread tid takes keys 4 tid + 4096 i .. + 3 with 16-byte LDS reads
     // (staged keys past T, up to the next multiple of 16, are 0: skipped)
 #pragma unroll
@@ -502,6 +502,10 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
         hist[b] = c;
       }
       __syncthreads();
+    }
+    if (tid >= 64 && pass < 2) {   // the next pass's histogram (used two passes ago)
+      const uint32_t nb_next = pass == 1 ? 1024u : 2048u;
+      for (uint32_t b = tid - 64; b < nb_next; b += kOneThreads - 64) hist2[(pass + 1) & 1][b] = 0;
     }
     if (tid < 64) {
       // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys),
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     mask = s_state[1];
     need = s_state[2];
     const bool resolved = s_state[3] != 0;
-    __syncthreads();   // s_state may be rewritten by the next pass
+    // no second barrier: the next pass writes the other histogram and state
     if (resolved) break;   // uniform across the workgroup
   }
 
