@@ -283,9 +283,10 @@ attn_bf16_kernel(
   __syncthreads();
 
   const int n_rounds = (t_end - t_first + KS - 1) / KS;
-  // one round; b is this round's buffer and nb the next one's.  Called with
-  // fixed buffers for even and odd rounds, so every LDS address of a round is
-  // a loop-invariant register plus an immediate.
+  // one round; b is this round's buffer and nb the next one's.  Unsplit at
+  // head dim <= 128 it is called with fixed buffers for even and odd rounds,
+  // so every LDS address of a round is a loop-invariant register plus an
+  // immediate.
   auto round = [&](const int j, const Smem& b, Smem& nb) __attribute__((always_inline)) {
     const int t = t_first + KS * j + kh;     // this stream's tile
     const int k0 = t * kBK;
@@ -407,12 +408,18 @@ attn_bf16_kernel(
     dma_wait();
     __syncthreads();
   };
-  int j = 0;
-  for (; j + 1 < n_rounds; j += 2) {
-    round(j, sm[0][kh], sm[1][kh]);
-    round(j + 1, sm[1][kh], sm[0][kh]);
+  if constexpr (D <= 128 && !SPLIT) {
+    int j = 0;
+    for (; j + 1 < n_rounds; j += 2) {
+      round(j, sm[0][kh], sm[1][kh]);
+      round(j + 1, sm[1][kh], sm[0][kh]);
+    }
+    if (j < n_rounds) round(j, sm[0][kh], sm[1][kh]);
+  } else {
+    // head dim 256, or a split chunk: three copies of the round would not
+    // fit the registers
+    for (int j = 0; j < n_rounds; ++j) round(j, sm[j & 1][kh], sm[(j + 1) & 1][kh]);
   }
-  if (j < n_rounds) round(j, sm[0][kh], sm[1][kh]);
   if (KS > 1) {
     // merge the streams' (running max, partial sums, O^T) into stream 0
     constexpr int NV = DB * 16 + 2;
