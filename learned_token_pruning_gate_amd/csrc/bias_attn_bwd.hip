@@ -35,6 +35,7 @@ namespace {
 
 constexpr int kTile = 64;          // keys per tile (dQ), queries per tile (dK/dV)
 constexpr int kKeysPerWg = 128;    // dK/dV: 4 waves x 32 keys
+constexpr int kMaxKvChunks = 8;    // dK/dV query chunks per key block, at most
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -633,6 +634,8 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_reduce_kernel(
   const int nq = (N + kTile - 1) / kTile;
   const int nc = kv_chunks(kb, nq, qchunk, causal != 0);
   if (nc <= 1) return;   // written directly by the key block's only workgroup
+  // (bandwidth-bound: occupancy hides the load latency, so the loop stays a
+  // plain one with few registers)
   f32x4 sk = f32x4{0.f, 0.f, 0.f, 0.f}, sv = sk;
   for (int c = 0; c < nc; ++c) {
     const size_t slot = (static_cast<size_t>(c) * nkb + kb) * Hkv + kvh;
@@ -667,11 +670,19 @@ __global__ __launch_bounds__(256) void attn_bwd_reduce_kernel(const float* __res
     const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
     if (i >= N) return;
     const int kb = static_cast<int>(i) / kKeysPerWg, kl = static_cast<int>(i) % kKeysPerWg;
-    const int nc = kv_chunks(kb, nq, qchunk, causal != 0);
+    const int nc = kv_chunks(kb, nq, qchunk, causal != 0);   // <= kMaxKvChunks
     float acc = 0.0f;
-    for (int h = 0; h < Hkv; ++h)
-      for (int c = 0; c < nc; ++c)
-        acc += part_ds[((static_cast<size_t>(c) * nkb + kb) * Hkv + h) * kKeysPerWg + kl];
+    for (int h = 0; h < Hkv; ++h) {
+      // a head's chunk partials read together, then added in chunk order
+      float v[kMaxKvChunks];
+#pragma unroll
+      for (int c = 0; c < kMaxKvChunks; ++c)
+        v[c] = c < nc ? part_ds[((static_cast<size_t>(c) * nkb + kb) * Hkv + h) * kKeysPerWg + kl]
+                      : 0.0f;
+#pragma unroll
+      for (int c = 0; c < kMaxKvChunks; ++c)
+        if (c < nc) acc += v[c];
+    }
     dscore[i] = acc;
     return;
   }
@@ -709,7 +720,8 @@ BwdWorkspace bwd_workspace(int64_t N, int64_t Hq, int64_t Hkv, int64_t D) {
   w.nkb = static_cast<int32_t>((N + kKeysPerWg - 1) / kKeysPerWg);
   const int64_t nq = (N + kTile - 1) / kTile;
   const int64_t pairs = std::max<int64_t>(int64_t{1}, w.nkb * Hkv);
-  const int64_t want = std::min<int64_t>(8, std::max<int64_t>(1, (768 + pairs - 1) / pairs));
+  const int64_t want =
+      std::min<int64_t>(kMaxKvChunks, std::max<int64_t>(1, (768 + pairs - 1) / pairs));
   w.qchunk = static_cast<int32_t>(std::max<int64_t>(1, (nq + want - 1) / want));
   w.nchunk = static_cast<int32_t>(std::max<int64_t>(1, (nq + w.qchunk - 1) / w.qchunk));
   const size_t slots = static_cast<size_t>(w.nchunk) * w.nkb * Hkv;
