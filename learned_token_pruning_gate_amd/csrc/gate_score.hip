@@ -315,10 +315,12 @@ __global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
 //     block (row-major fragments gather 16 rows 4 KiB apart);
 //   * LDS traffic per stage is the tile written once and read by each wave:
 //     (1 + NW) * 8 KiB, against 16 MFMAs per wave.
-// The compiler does not track the direct loads, so waits are explicit: a wave
-// waits for its own loads of stage s (s_waitcnt vmcnt), then one barrier per
-// stage makes every wave's stage visible and frees the slot of stage s-1.
-// The row's sum of squares comes from the A fragments read back.
+// The compiler does not track the direct loads, so waits are explicit.  The
+// A fragments are read one stage ahead: during stage s a wave waits for its
+// own loads of stage s+1 (s_waitcnt vmcnt), one barrier makes every wave's
+// stage s+1 visible (and frees the slot of stage s-1), and the wave reads
+// stage s+1's fragments before issuing stage s's MFMAs, whose fragments it
+// read in stage s-1.  The row's sum of squares comes from the A fragments.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
   return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14);   // lgkmcnt/expcnt: no wait
