@@ -241,14 +241,17 @@ tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
  * short for its workgroups to fill the chip, the longest causal rows alone
  * set the time; with a workspace the call cuts every long row's key tiles
  * into chunks run by separate workgroups, each chunk keeps the online-softmax
- * state (running max, sum, unnormalised output) of its keys, and a second
- * kernel combines the chunks of each row exactly as the online softmax
- * combines key tiles.
+ * state of its keys (running max and sum in fp32; the unnormalised output
+ * scaled by a power of two folded into the max, and rounded to fp16), and a
+ * second kernel combines the chunks of each row as the online softmax
+ * combines key tiles.  A cost model decides per shape whether
+ * the split pays.
  *
  * tg_bias_attn_workspace_size  bytes the split needs for this shape, or 0
- *           when the shape runs unsplit (fp32, head dim 256, a grid that
- *           fills the chip, or rows too short to cut).  Depends only on the
- *           arguments; invalid arguments also give 0.
+ *           when the shape runs unsplit (fp32, a grid that fills the chip,
+ *           rows too short to cut, or a split the cost model prices above
+ *           the unsplit launch).  Depends only on the arguments; invalid
+ *           arguments also give 0.
  * workspace device memory of at least that many bytes, 16-byte aligned, or
  *           NULL: the call then runs unsplit, as tg_bias_attn_fwd.  Needs no
  *           initialisation; left undefined.  Calls sharing a workspace must

@@ -132,7 +132,7 @@ constexpr int kMaxBins = 512;     // workgroups per query-head group
 constexpr int kMaxItems = 1024;   // items per query-head group
 
 struct SplitArgs {
-  float* part_o;    // [slot][4 waves][D/32][64 lanes][16] f32: O^T accumulators
+  uint16_t* part_o;   // [slot][4 waves][D/32][64 lanes][16] fp16: scaled O^T accumulators
   float* part_ml;   // [slot][4 waves][64 lanes][2] f32: running max (log2 units), sum
   // slot of chunk c of split row p: ((npb - 1 - p) * nchunk + c) * query-head groups + group
   int32_t ctiles;   // C, key tiles per chunk
@@ -457,15 +457,33 @@ attn_bf16_kernel(
   if constexpr (SPLIT) {
     if (slot != kNoSlot) {
       // one chunk of a split row: hand the unnormalised state to the merge
-      const size_t ws = slot * 4 + wave;
-      float* po = sp.a.part_o + (ws * DB * 64 + lane) * 16;
+      // O^T goes out in fp16 (half the bytes written here and read by the
+      // merge).  The state (m, l, O) and (m - k, l 2^k, O 2^k) stand for the
+      // same weights 2^(y - m), so each lane scales its O by the power of two
+      // 2^k that puts its largest |O| in [2^14, 2^15): no fp16 overflow, and
+      // one rounding of 2^-11 relative.  The max and sum stay fp32.
+      float amax = 0.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4*>(po + db * 64 * 16 + 4 * j) =
-              f32x4{o[db][4 * j], o[db][4 * j + 1], o[db][4 * j + 2], o[db][4 * j + 3]};
-      *reinterpret_cast<float2*>(sp.a.part_ml + ws * 128 + 2 * lane) = make_float2(m_run, l_tot);
+        for (int r = 0; r < 16; ++r) amax = fmaxf(amax, fabsf(o[db][r]));
+      int e = 0;
+      (void)frexpf(amax, &e);                       // amax < 2^e (amax == 0: e == 0)
+      const int k = amax > 0.0f ? min(max(15 - e, -60), 60) : 0;
+      const float sc = ldexpf(1.0f, k);
+      const size_t ws = slot * 4 + wave;
+      uint16_t* po = sp.a.part_o + (ws * DB * 64 + lane) * 16;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int h8 = 0; h8 < 2; ++h8) {
+          f16x8 w;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) w[i] = static_cast<_Float16>(o[db][8 * h8 + i] * sc);
+          *reinterpret_cast<f16x8*>(po + db * 64 * 16 + 8 * h8) = w;
+        }
+      *reinterpret_cast<float2*>(sp.a.part_ml + ws * 128 + 2 * lane) =
+          make_float2(m_run == -INFINITY ? m_run : m_run - static_cast<float>(k), l_tot * sc);
       return;
     }
   }
@@ -540,16 +558,16 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SplitArgs sp, uint16_t*
 
   // every load first (one round trip), then the combination
   float2 ml[kMaxChunks];
-  f32x4 ov[kMaxChunks][4];
+  f16x8 ov[kMaxChunks][2];
 #pragma unroll
   for (int c = 0; c < kMaxChunks; ++c) {
     if (c < nc) {
       const size_t slot = ((static_cast<size_t>(rank) * sp.nchunk + c) * n_hgroups + hg) * 4 + wave;
       ml[c] = *reinterpret_cast<const float2*>(sp.part_ml + slot * 128 + 2 * lane);
-      const f32x4* po =
-          reinterpret_cast<const f32x4*>(sp.part_o + ((slot * DB + db) * 64 + lane) * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ov[c][j] = po[j];
+      const f16x8* po =
+          reinterpret_cast<const f16x8*>(sp.part_o + ((slot * DB + db) * 64 + lane) * 16);
+      ov[c][0] = po[0];
+      ov[c][1] = po[1];
     }
   }
   float m_max = -INFINITY;
@@ -568,7 +586,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SplitArgs sp, uint16_t*
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[j][i] = fmaf(w, ov[c][j][i], acc[j][i]);
+        for (int i = 0; i < 4; ++i)
+          acc[j][i] = fmaf(w, static_cast<float>(ov[c][j >> 1][4 * (j & 1) + i]), acc[j][i]);
     }
   }
   const bool empty = !(l_tot > 0.0f) || m_max == -INFINITY;
@@ -677,7 +696,7 @@ struct AttnArgs {
 // Key-chunk split of a bf16 launch (ctiles == 0: the launch runs unsplit).
 struct SplitPlan {
   int32_t ctiles = 0, nchunk = 0, n_bins = 0, n_split_rows = 0;
-  size_t part_o_floats = 0, bytes = 0;
+  size_t part_o_elems = 0, bytes = 0;   // bf16 elements of part_o; workspace bytes
   std::vector<uint16_t> bin_first, items;
 };
 
@@ -718,7 +737,9 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
       tasks.push_back((D <= 128 ? (nt + 1) / 2 * kTwoStreamRoundUnits : nt) + kItemUnits);
     }
   double best = list_schedule(tasks, kCUs) * kSplitGain;
-  const size_t state_bytes = static_cast<size_t>(4) * ((D / 32) * 16 * 64 + 128) * sizeof(float);
+  // per state slot (4 waves): O^T in fp16, (max, sum) in fp32
+  const size_t state_bytes =
+      static_cast<size_t>(4) * ((D / 32) * 16 * 64 * sizeof(uint16_t) + 128 * sizeof(float));
   struct Item {
     int size, p, c;
   };
@@ -782,7 +803,7 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
   }
   if (best_plan.ctiles == 0) return best_plan;
   const size_t n_states = static_cast<size_t>(best_plan.n_split_rows) * best_plan.nchunk * nhg;
-  best_plan.part_o_floats = n_states * 4 * (D / 32) * 16 * 64;
+  best_plan.part_o_elems = n_states * 4 * (D / 32) * 16 * 64;
   best_plan.bytes = n_states * state_bytes;
   return best_plan;
 }
@@ -825,8 +846,8 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
   {
     if (pl.ctiles > 0 && workspace != nullptr) {
       SplitLaunch sl{};
-      sl.a.part_o = static_cast<float*>(workspace);
-      sl.a.part_ml = sl.a.part_o + pl.part_o_floats;
+      sl.a.part_o = static_cast<uint16_t*>(workspace);
+      sl.a.part_ml = reinterpret_cast<float*>(sl.a.part_o + pl.part_o_elems);
       sl.a.ctiles = pl.ctiles;
       sl.a.nchunk = pl.nchunk;
       std::copy(pl.bin_first.begin(), pl.bin_first.end(), sl.bin_first);

@@ -195,10 +195,11 @@ def test_attn_workspace_size(lib):
     # rows of 32 queries (row p has ceil(32 (p + 1) / 64) key tiles) x 2 head
     # groups; the plan cuts rows into chunks of 15 tiles, so rows 30..78 (49
     # rows) are split, with state slots for 3 chunks per head group: 49 x 3 x
-    # 2 slots of 4 waves x (8 x 16 x 64 + 128) floats
-    assert size(BF16, 2512, 8, 2, 256, 1) == 49 * 3 * 2 * 4 * (8 * 16 * 64 + 128) * 4
-    # the same prompt at 16/8 heads, D = 128: two key streams beat the split
-    assert size(BF16, 2512, 16, 8, 128, 1) == 0
+    # 2 slots of 4 waves x (8 x 16 x 64 fp16 of O^T + 128 floats of max, sum)
+    assert size(BF16, 2512, 8, 2, 256, 1) == 49 * 3 * 2 * 4 * (8 * 16 * 64 * 2 + 128 * 4)
+    # the same prompt at 16/8 heads, D = 128: with fp16 chunk states the split
+    # is priced below the two-stream launch
+    assert size(BF16, 2512, 16, 8, 128, 1) > 0
     assert size(F32, 2512, 16, 8, 128, 1) == 0          # fp32 path never splits
     assert size(BF16, 32768, 16, 8, 128, 1) == 0        # grid fills the chip
     assert size(BF16, 100, 16, 8, 128, 1) == 0          # rows too short to cut
