@@ -369,6 +369,29 @@ def main():
     roof["kernel"] = dominant
     roof["traffic"] = load_traffic(dominant)
 
+    # cost of the bias path: the attention call alone, with the step's key-score
+    # bias and per-query scale, against the same call with both left out (a
+    # plain causal GQA flash attention); the pages put the biased call at
+    # 1.0-1.1x the plain one
+    def time_attn(a_args, reps):
+        for _ in range(2):
+            check(lib.tg_bias_attn_fwd_ws(*a_args), "tg_bias_attn_fwd_ws")
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        b0.record(stream)
+        for _ in range(reps):
+            check(lib.tg_bias_attn_fwd_ws(*a_args), "tg_bias_attn_fwd_ws")
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) * 1e3 / reps
+
+    plain_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), None, None, None,
+                  F(0.0), 1, P(out), P(lse), P(att_ws), att_ws_bytes, sp)
+    reps = max(args.steps, 10)
+    with_us, plain_us = time_attn(att_args, reps), time_attn(plain_args, reps)
+    bias_cost = {"with_bias_us": with_us, "plain_us": plain_us, "ratio": with_us / plain_us,
+                 "calls": reps, "pages_ratio": "1.0-1.1"}
+
     # attention backward (the gate's training path), timed on its own: not
     # part of the prefill step
     bwd_info = None
@@ -431,6 +454,7 @@ def main():
         "roofline": roof,
         "stages": stage_info,
         "attn_bwd": bwd_info,
+        "attn_bias_cost": bias_cost,
     }
     if cold:
         result["cold_stage_ms"] = cold
