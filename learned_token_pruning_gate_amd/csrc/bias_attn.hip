@@ -56,6 +56,7 @@
 #include <algorithm>
 #include <deque>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <queue>
 #include <type_traits>
@@ -696,7 +697,7 @@ struct AttnArgs {
 // Key-chunk split of a bf16 launch (ctiles == 0: the launch runs unsplit).
 struct SplitPlan {
   int32_t ctiles = 0, nchunk = 0, n_bins = 0, n_split_rows = 0;
-  size_t part_o_elems = 0, bytes = 0;   // bf16 elements of part_o; workspace bytes
+  size_t part_o_elems = 0, bytes = 0;   // fp16 elements of part_o; workspace bytes
   std::vector<uint16_t> bin_first, items;
 };
 
@@ -808,19 +809,26 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
   return best_plan;
 }
 
-// Plans depend only on the shape; the few shapes a process uses are kept.
-const SplitPlan& split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal) {
+// Plans depend only on the shape and are kept for the last kPlanCache shapes
+// (the kept-token count N changes from prompt to prompt, so the cache is
+// bounded; the oldest entry goes first).  A caller holds its plan through a
+// shared pointer, so an eviction by another thread never frees it early.
+constexpr size_t kPlanCache = 256;
+std::shared_ptr<const SplitPlan> split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
+                                            bool causal) {
   struct Entry {
     int64_t N, Hq, Hkv, D;
     bool causal;
-    SplitPlan plan;
+    std::shared_ptr<const SplitPlan> plan;
   };
   static std::mutex mu;
-  static std::deque<Entry> cache;   // entries are never erased: references stay valid
+  static std::deque<Entry> cache;
   std::lock_guard<std::mutex> lock(mu);
   for (const Entry& e : cache)
     if (e.N == N && e.Hq == Hq && e.Hkv == Hkv && e.D == D && e.causal == causal) return e.plan;
-  cache.push_back(Entry{N, Hq, Hkv, D, causal, make_split_plan(N, Hq, Hkv, D, causal)});
+  if (cache.size() >= kPlanCache) cache.pop_front();
+  cache.push_back(Entry{N, Hq, Hkv, D, causal,
+                        std::make_shared<const SplitPlan>(make_split_plan(N, Hq, Hkv, D, causal))});
   return cache.back().plan;
 }
 
@@ -911,7 +919,9 @@ tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, c
                 "tg_bias_attn_fwd: bf16 path addresses Q/K/V with 32-bit offsets "
                 "(N * Hq * D * 2 must be < 2^31)");
   static const SplitPlan kUnsplit;
-  const SplitPlan& pl = dt == TG_DTYPE_BF16 ? split_plan(N, Hq, Hkv, D, causal != 0) : kUnsplit;
+  const std::shared_ptr<const SplitPlan> plan =
+      dt == TG_DTYPE_BF16 ? split_plan(N, Hq, Hkv, D, causal != 0) : nullptr;
+  const SplitPlan& pl = plan ? *plan : kUnsplit;
   if (workspace != nullptr) {
     if (!aligned(workspace, 16))
       return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd_ws: workspace must be 16-byte aligned");
@@ -994,7 +1004,7 @@ extern "C" size_t tg_bias_attn_workspace_size(tg_dtype dt, int64_t N, int64_t Hq
   if (dt != TG_DTYPE_BF16 || N <= 0 || N > tg::kMaxTokens || Hq < 1 || Hkv < 1 ||
       Hq % Hkv != 0 || (D != 64 && D != 128 && D != 256) || N * Hq * D * 2 > tg::kMaxTokens)
     return 0;
-  return tg::split_plan(N, Hq, Hkv, D, causal != 0).bytes;
+  return tg::split_plan(N, Hq, Hkv, D, causal != 0)->bytes;
 }
 
 extern "C" tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,

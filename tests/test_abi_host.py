@@ -209,6 +209,17 @@ def test_attn_workspace_size(lib):
     assert size(BF16, 2512, 16, 8, 128, 0) > 0          # non-causal rows split too
 
 
+def test_attn_plan_cache_is_bounded(lib):
+    # the kept-token count changes from prompt to prompt: 300 distinct shapes
+    # overflow the plan cache (256 shapes), and a plan computed again after
+    # its eviction sizes the workspace the same way
+    size = lambda n: lib.tg_bias_attn_workspace_size(BF16, n, 16, 8, 128, 1)
+    first = {n: size(n) for n in range(1200, 4200, 10)}
+    assert any(v > 0 for v in first.values())
+    for n in (1200, 2510, 4190):
+        assert size(n) == first[n]
+
+
 def test_attn_ws_validation(lib):
     need = lib.tg_bias_attn_workspace_size(BF16, 2512, 16, 8, 128, 0)   # non-causal splits
     assert _attn_ws(lib, FAKE, 0) == WS
