@@ -174,8 +174,8 @@ def main():
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build measures one GPU only (the path runs on one "
-              "MI355X; multi-GPU sharding is a design note, not built); use --gpus 1",
+        print("bench.py: only one GPU is measured (the path runs on one MI355X; "
+              "sharding across GPUs is designed but not built); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 
