@@ -275,6 +275,23 @@ def test_product_binding_refuses_cpu_tensors():
         tg.tg_gate_score(x, torch.ones(4, dtype=torch.uint8), x, torch.zeros(4))
 
 
+def test_product_binding_fails_loudly_without_the_library():
+    # no fallback: with the library missing, loading raises and says how to build
+    code = ("import learned_token_pruning_gate_amd as tg\n"
+            "tg.lib_path = '/nonexistent/libtokengate.so'\n"
+            "tg._lib = None\n"
+            "try:\n"
+            "    tg.load()\n"
+            "except RuntimeError as e:\n"
+            "    print('raised:', e)\n")
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert "raised: libtokengate.so is not built" in r.stdout
+
+
 def test_product_package_does_not_import_the_oracle():
     src_dir = os.path.join(ROOT, "learned_token_pruning_gate_amd")
     for dirpath, _, files in os.walk(src_dir):
