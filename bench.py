@@ -6,7 +6,14 @@ over the N kept tokens (one gate plus one upper attention layer).  Inputs
 are seeded synthetic tensors of the workload's shapes, resident in HBM
 before the timed region; outputs are preallocated.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t16k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload t32k-dense]
+
+The default workload is the dense 32k prompt (T = 32768, every token kept,
+16/8 heads, head dim 128): the compute-bound configuration on which the
+attention's share of the MFMA peak is quoted.  The same run also times the
+other bf16 prompts (16k, 32k with K = 100/500/2000, 128k) and reports each
+one's step time and per-stage times under "other_workloads" (--no-others
+skips them).
 
 By default each timed step is one replay of the four calls captured as a HIP
 graph (tg_chain_create); --mode eager launches them one by one.  Per-stage
@@ -63,17 +70,31 @@ def algorithmic(w, N, kv_layers=0):
     }
 
 
-def load_traffic(stage):
+def load_traffic(workload, stage):
     """HBM bytes per launch measured by rocprofv3 --pmc (FETCH_SIZE and
-    WRITE_SIZE, scaled by a copy-kernel calibration), if recorded for the
-    current kernel source; None otherwise."""
+    WRITE_SIZE, scaled by a copy-kernel calibration) for this workload and
+    stage, if recorded for the current kernel source; None otherwise."""
     p = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(p):
         return None
-    rec = json.load(open(p)).get(stage)
+    rec = json.load(open(p)).get(workload, {}).get(stage)
     if not rec or rec.get("source_sha") != source_sha(stage):
         return None
     return rec.get("bytes_per_launch")
+
+
+def host_cpu():
+    """(CPU model, OMP_NUM_THREADS as set or None) of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.environ.get("OMP_NUM_THREADS")
 
 
 def cpu_baseline(w, g, a, N, kept, scores_gpu, key_score):
@@ -122,9 +143,11 @@ def cpu_baseline(w, g, a, N, kept, scores_gpu, key_score):
     total = t_gate + t_sel + t_gat + t_att
     sample_s = t_gate_sample + t_sel + t_gat + t_att_sample
     threads = oracle.num_threads()
+    model, omp = host_cpu()
     return {
         "value": T / total, "unit": "tokens/s", "cores": threads,
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": model, "omp_num_threads": omp,
+        "nproc": os.cpu_count(),
         "sample": ("fp64 C oracle on this host: gate on %d of %d prunable rows, full top-K "
                    "and gather, attention on %d of %d query rows (all heads); each stage "
                    "scaled to the full step by its row count (attention by causal work); "
@@ -135,12 +158,19 @@ def cpu_baseline(w, g, a, N, kept, scores_gpu, key_score):
     }
 
 
-def main():
+
+
+OTHER_WORKLOADS = ("t16k", "t32k-K100", "t32k-K500", "t32k-K2000", "t128k")
+
+
+def parse_args(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="t16k")
+    ap.add_argument("--workload", default="t32k-dense")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the step and stage times of the other bf16 workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps with the last-level cache flushed before each")
@@ -172,20 +202,21 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy, the reference kernel that "
                          "scales FETCH_SIZE / WRITE_SIZE counter readings to bytes")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py: only one GPU is measured (the path runs on one MI355X; "
-              "sharding across GPUs is designed but not built); use --gpus 1",
-              file=sys.stderr)
-        sys.exit(2)
+    return ap.parse_args(argv)
 
+
+def run_workload(w, args, full):
+    """Times the path on one workload.  full=False: the graph-replayed step
+    and the per-stage events only (the other workloads' lines); full=True:
+    also the bias self-check, the backward, the cold-cache stages and the
+    CPU oracle baseline."""
     import numpy as np
     import torch
 
     import learned_token_pruning_gate_amd as tg
     import workloads
 
-    w = workloads.get(args.workload)
+    print("bench: workload %s" % w.name, file=sys.stderr, flush=True)
     g, a = workloads.generate(w)
     N = w.n_kept
     dev = torch.device("cuda", 0)
@@ -255,7 +286,7 @@ def main():
                                                      tg.tg_last_error()))
 
     stages = ["gate", "select", "gather", "attn"]
-    kvl = args.kv_layers
+    kvl = args.kv_layers if full else 0
     if kvl > 0:
         kv_k = torch.randn((kvl, w.T, w.Hkv, w.D), device=dev).to(q.dtype)
         kv_v = torch.randn((kvl, w.T, w.Hkv, w.D), device=dev).to(q.dtype)
@@ -295,7 +326,7 @@ def main():
         if kvl > 0:
             stream.wait_event(join_ev)
 
-    if args.copy_calibration:
+    if full and args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -367,7 +398,21 @@ def main():
         roof = {"bound": "hbm", "achieved": di["GB_s"], "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": di["hbm_frac"]}
     roof["kernel"] = dominant
-    roof["traffic"] = load_traffic(dominant)
+    roof["traffic"] = load_traffic(w.name, dominant)
+
+    config = {"workload": w.name, "T": w.T, "d": w.d, "h": w.h,
+              "n_prunable": w.n_prunable, "K": w.K, "N_kept": N, "Hq": w.Hq,
+              "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
+              "gate_w1": "packed" if use_packed else "row-major",
+              "kv_layers": kvl, "attn_split": att_ws is not None,
+              "parallelism": "single-gpu"}
+    if not full:
+        return {"config": config, "ms_per_step": ms_per_step, "tokens_per_s": value,
+                "eager_ms_per_step": eager_ms, "graph_ms_per_step": graph_ms,
+                "stage_ms": per_stage_ms,
+                "attn_frac_of_peak": stage_info["attn"].get("mfma_frac"),
+                "gate_hbm_frac": stage_info["gate"]["hbm_frac"],
+                "gather_hbm_frac": stage_info["gather"]["hbm_frac"]}
 
     # cost of the bias path: the attention call alone, with the step's key-score
     # bias and per-query scale, against the same call with both left out (a
@@ -376,18 +421,18 @@ def main():
     def time_attn(a_args, reps):
         for _ in range(2):
             check(lib.tg_bias_attn_fwd_ws(*a_args), "tg_bias_attn_fwd_ws")
-        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0, b1_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         b0.record(stream)
         for _ in range(reps):
             check(lib.tg_bias_attn_fwd_ws(*a_args), "tg_bias_attn_fwd_ws")
-        b1.record(stream)
+        b1_.record(stream)
         torch.cuda.synchronize()
-        return b0.elapsed_time(b1) * 1e3 / reps
+        return b0.elapsed_time(b1_) * 1e3 / reps
 
     plain_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), None, None, None,
                   F(0.0), 1, P(out), P(lse), P(att_ws), att_ws_bytes, sp)
-    reps = max(args.steps, 10)
+    reps = max(min(args.steps, 20), 5)
     with_us, plain_us = time_attn(att_args, reps), time_attn(plain_args, reps)
     bias_cost = {"with_bias_us": with_us, "plain_us": plain_us, "ratio": with_us / plain_us,
                  "calls": reps, "pages_ratio": "1.0-1.1"}
@@ -407,21 +452,22 @@ def main():
         bwd_args = (dtc, N, w.Hq, w.Hkv, w.D, P(q), P(k), P(v), key_ptr, P(gain), P(q_scale),
                     F(0.0), 1, P(out), P(dout), P(lse), P(dq_), P(dk_), P(dv_), P(dscore_),
                     P(dgain_), P(bws), bws.numel(), sp)
-        for _ in range(2):
-            check(lib.tg_bias_attn_bwd(*bwd_args), "tg_bias_attn_bwd")
+        check(lib.tg_bias_attn_bwd(*bwd_args), "tg_bias_attn_bwd")
+        bwd_calls = max(min(args.steps, 10), 3)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record(stream)
-        for _ in range(args.steps):
+        for _ in range(bwd_calls):
             check(lib.tg_bias_attn_bwd(*bwd_args), "tg_bias_attn_bwd")
         e1.record(stream)
         torch.cuda.synchronize()
-        bwd_ms = e0.elapsed_time(e1) / args.steps
+        bwd_ms = e0.elapsed_time(e1) / bwd_calls
         bwd_flops = 5 * w.D * w.Hq * N * (N + 1)   # S, dP, dV, dK, dQ products (causal)
         bwd_info = {"ms": bwd_ms, "flops": bwd_flops,
                     "TFLOP_s": bwd_flops / (bwd_ms * 1e-3) / 1e12,
                     "mfma_frac": bwd_flops / (bwd_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-                    "calls": args.steps}
+                    "calls": bwd_calls}
+        del dout, dq_, dk_, dv_, bws
 
     cold = None
     if args.cold:
@@ -440,12 +486,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": w.name, "T": w.T, "d": w.d, "h": w.h,
-                   "n_prunable": w.n_prunable, "K": w.K, "N_kept": N, "Hq": w.Hq,
-                   "Hkv": w.Hkv, "D": w.D, "causal": True, "global_batch": 1,
-                   "gate_w1": "packed" if use_packed else "row-major",
-                   "kv_layers": kvl, "attn_split": att_ws is not None,
-                   "parallelism": "single-gpu"},
+        "config": config,
         "mode": args.mode,
         "eager_ms_per_step": eager_ms,
         "graph_ms_per_step": graph_ms,
@@ -460,10 +501,36 @@ def main():
         result["cold_stage_ms"] = cold
 
     if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle) on a sample of %s" % w.name, file=sys.stderr,
+              flush=True)
         kept_host = kept.cpu().numpy()[:N]
         key_host = (drawn if drawn is not None else score_kept).cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, g, a, N, kept_host, scores.cpu().numpy(),
                                               key_host)
+    return result
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py: only one GPU is measured (the path runs on one MI355X; "
+              "sharding across GPUs is designed but not built); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads
+
+    result = run_workload(workloads.get(args.workload), args, full=True)
+    if not args.no_others:
+        others = {}
+        for name in OTHER_WORKLOADS:
+            if name == args.workload:
+                continue
+            others[name] = run_workload(workloads.get(name), args, full=False)
+            torch.cuda.empty_cache()
+        result["other_workloads"] = others
     print(json.dumps(result))
 
 

@@ -23,9 +23,16 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * - Every data pointer is DEVICE memory owned by the caller.  The library
- *   allocates nothing and keeps no per-call state; the only scratch memory
- *   is the caller-provided workspace of tg_topk_select.
+ * - Every data pointer is DEVICE memory owned by the caller.  The compute
+ *   calls allocate no device memory; their scratch memory is caller-provided
+ *   workspace, sized by a query: tg_topk_select's (tg_topk_workspace_size),
+ *   the split attention's (tg_bias_attn_workspace_size) and the backward's
+ *   (tg_bias_attn_bwd_workspace_size).  Only tg_chain_create allocates (the
+ *   runtime's graph objects).
+ * - Host-side state: the split attention's plans depend only on the shape
+ *   and are kept in a bounded cache of the last 256 shapes, guarded by a
+ *   mutex, so every call is thread-safe; the device properties are read
+ *   once per device.
  * - Every call only enqueues work on `stream` (a hipStream_t; NULL means the
  *   null stream) and returns; nothing synchronises the device and nothing
  *   is read back to the host.  Results are valid once the stream reaches
@@ -222,7 +229,8 @@ tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
  * gain          [Hq] f32, required when key_score != NULL.  Expected > 0
  *               (a softplus output); gain 0 with an infinite score is NaN.
  * q_scale       [N] f32 per-query logit scale, or NULL for all ones.
- *               Expected > 0.
+ *               Expected > 0.  A -inf key_score deletes its key exactly
+ *               whenever softmax_scale * q_scale[r] > 2^-80.
  * softmax_scale <= 0 selects 1/sqrt(D).
  * causal        nonzero: key c is visible to query r only if c <= r.
  * out           out [N][Hq][D] of dt.  lse: out [Hq][N] f32, or NULL.

@@ -64,10 +64,6 @@
 
 #include "tg_common.hpp"
 
-#ifndef TG_ATTN_QW8
-#define TG_ATTN_QW8 1
-#endif
-
 namespace tg {
 namespace {
 
@@ -192,10 +188,12 @@ attn_bf16_kernel(
 
   // ---- staging -------------------------------------------------------------
   const float inv_scale = 1.0f / scale;
-  // A -inf score becomes a bias of -2^21 log2 units (in dot-product units):
-  // for any per-query scale >= 0.25 the logit falls below kMaskedLog2 and its
-  // weight underflows to exactly 0, as deleting the key would give.
-  const float masked_bias = -2097152.0f * inv_scale / kLog2e;
+  // A -inf score becomes the bias -2^100 in dot-product units (exact in
+  // bf16, so the bias k-step adds it exactly and it absorbs any finite dot
+  // product).  Its logit, -2^100 scale log2(e) c_r log2 units, falls below
+  // kMaskedLog2 whenever scale * c_r > 2^-80, and its weight underflows to
+  // exactly 0, as deleting the key would give.
+  const float masked_bias = -0x1p100f;
   float sreg = 0.0f;        // staged raw score (its bias is formed at store time)
   const int bias_key = tid % kBK;
   const float bias_gain = (HAS_BIAS && tid < HPW * kBK) ? gain[hg * HPW + tid / kBK] : 0.0f;
@@ -665,10 +663,10 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 // cost of a whole CU's LDS per workgroup: they pay off while the grid is too
 // small to keep every CU busy with one-stream workgroups for several rounds.
 constexpr int64_t kTwoStreamMaxGrid = 1024;
-// Workgroups resident at once on the chip (256 CUs): two per CU for the
-// one-stream kernel at head dim <= 128, one per CU for two-stream workgroups
-// and at head dim 256 (whose tile pair fills a CU's LDS).
-constexpr int kCUs = 256;
+// Workgroups resident at once on the chip (its compute units, 256 on
+// MI355X, read from the device): two per CU for the one-stream kernel at
+// head dim <= 128, one per CU for two-stream workgroups and at head dim 256
+// (whose tile pair fills a CU's LDS).
 constexpr int kMinChunkTiles = 4;
 // Cost model, in units of one key tile of one workgroup (~2.4 us at head
 // dim 128 with two workgroups per CU): each item adds its setup (Q and first
@@ -716,7 +714,8 @@ double list_schedule(const std::vector<double>& tasks, int slots) {
   return end;
 }
 
-SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal) {
+SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool causal,
+                          int cus) {
   SplitPlan best_plan;
   if (N <= 0) return best_plan;
   const int64_t G = Hq / Hkv;
@@ -726,7 +725,7 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
   if (static_cast<int64_t>(npb) * nhg > kTwoStreamMaxGrid) return best_plan;
   const int n = static_cast<int>(N);
   const int nt_max = row_tiles(npb - 1, PB, n, causal);
-  const int slots = D <= 128 ? 2 * kCUs : kCUs;   // split workgroups resident at once
+  const int slots = D <= 128 ? 2 * cus : cus;   // split workgroups resident at once
   const int max_bins = std::min(kMaxBins, slots / nhg);
   if (max_bins < 1) return best_plan;
   // unsplit: at head dim <= 128 two key streams per workgroup, each walking
@@ -737,7 +736,7 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
       const int nt = row_tiles(p, PB, n, causal);
       tasks.push_back((D <= 128 ? (nt + 1) / 2 * kTwoStreamRoundUnits : nt) + kItemUnits);
     }
-  double best = list_schedule(tasks, kCUs) * kSplitGain;
+  double best = list_schedule(tasks, cus) * kSplitGain;
   // per state slot (4 waves): O^T in fp16, (max, sum) in fp32
   const size_t state_bytes =
       static_cast<size_t>(4) * ((D / 32) * 16 * 64 * sizeof(uint16_t) + 128 * sizeof(float));
@@ -819,16 +818,21 @@ std::shared_ptr<const SplitPlan> split_plan(int64_t N, int64_t Hq, int64_t Hkv, 
   struct Entry {
     int64_t N, Hq, Hkv, D;
     bool causal;
+    int cus;
     std::shared_ptr<const SplitPlan> plan;
   };
+  const int cus = device_cu_count();
   static std::mutex mu;
   static std::deque<Entry> cache;
   std::lock_guard<std::mutex> lock(mu);
   for (const Entry& e : cache)
-    if (e.N == N && e.Hq == Hq && e.Hkv == Hkv && e.D == D && e.causal == causal) return e.plan;
+    if (e.N == N && e.Hq == Hq && e.Hkv == Hkv && e.D == D && e.causal == causal &&
+        e.cus == cus)
+      return e.plan;
   if (cache.size() >= kPlanCache) cache.pop_front();
-  cache.push_back(Entry{N, Hq, Hkv, D, causal,
-                        std::make_shared<const SplitPlan>(make_split_plan(N, Hq, Hkv, D, causal))});
+  cache.push_back(Entry{N, Hq, Hkv, D, causal, cus,
+                        std::make_shared<const SplitPlan>(
+                            make_split_plan(N, Hq, Hkv, D, causal, cus))});
   return cache.back().plan;
 }
 
@@ -875,7 +879,6 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
       launch_bf16_attn_ks<D, HPW, CAUSAL, 2, false>(a, grid, npb, nhg, none);
       return;
     }
-#if TG_ATTN_QW8
     // large grids: 8-wave workgroups, two query blocks sharing each staged
     // key tile (half the staging work per wave at the same occupancy)
     constexpr int PB8 = 32 * (8 / HPW);
@@ -883,7 +886,6 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
     launch_bf16_attn_ks<D, HPW, CAUSAL, 1, false, NoSplit, 8>(
         a, dim3(static_cast<uint32_t>(static_cast<int64_t>(npb8) * nhg)), npb8, nhg, none);
     return;
-#endif
   }
   launch_bf16_attn_ks<D, HPW, CAUSAL, 1, false>(a, grid, npb, nhg, none);
 }

@@ -246,7 +246,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
                                               : u32x4{0, 0, 0, 0});
 
   const float inv_scale = 1.0f / scale;
-  const float masked_bias = -2097152.0f * inv_scale / kLog2e;
+  // a -inf score: -2^100 in dot-product units absorbs any finite dot product,
+  // and its weight underflows to exactly 0 whenever scale * c_r > 2^-80
+  const float masked_bias = -0x1p100f;
   const int bias_key = tid % kTile;
   const float bias_gain = (HAS_BIAS && tid < HPW * kTile) ? gain[hg * HPW + tid / kTile] : 0.0f;
   const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
@@ -430,7 +432,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   }
   const float s_key = (HAS_BIAS && k_ok) ? key_score[my_k] : 0.0f;
   const float inv_scale = 1.0f / scale;
-  const float masked_bias = -2097152.0f * inv_scale / kLog2e;
+  // a -inf score: -2^100 in dot-product units absorbs any finite dot product,
+  // and its weight underflows to exactly 0 whenever scale * c_r > 2^-80
+  const float masked_bias = -0x1p100f;
   // the query side of the bias k-step: [1, 1, 1, 0 ...] in the hh = 0 half
   const bf16x8 ones = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
                                                          : u32x4{0, 0, 0, 0});

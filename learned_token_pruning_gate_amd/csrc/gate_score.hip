@@ -32,19 +32,15 @@ namespace tg {
 namespace {
 
 constexpr int kKS = 64;                 // k elements per stage
-#ifndef TG_GATE_TM
-#define TG_GATE_TM 64                   // residual rows per workgroup
-#endif
+constexpr int kTM = 64;                 // residual rows per workgroup (register-staged kernel)
 constexpr int kPitch = kKS + 8;         // LDS row pitch in bf16 (144 bytes)
 
-#ifndef TG_GATE_MINWG
-#define TG_GATE_MINWG 2                 // workgroups per CU the registers are sized for
-#endif
+constexpr int kMinWG = 2;               // workgroups per CU its registers are sized for
 
 // FAST: d is a multiple of 2 * kKS, so every stage is full; per-lane load
 // offsets are fixed and the stage advance is the instruction's scalar offset.
 template <int TM, int NT, bool HAS_GAMMA, bool FAST>
-__global__ __launch_bounds__(256, TG_GATE_MINWG) void gate_bf16_kernel(
+__global__ __launch_bounds__(256, kMinWG) void gate_bf16_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     const float* __restrict__ gamma, float eps, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2,
@@ -327,9 +323,7 @@ __device__ __forceinline__ constexpr int vmcnt_imm(int n) {
 }
 constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);    // lgkmcnt(0) only
 
-#ifndef TG_GATE_DEPTH
-#define TG_GATE_DEPTH 4                 // k-stages in flight in the streaming kernel
-#endif
+constexpr int kDepth = 4;               // k-stages in flight in the streaming kernel
 
 struct XSlot {
   u32x4 b[8][64];   // (row tile mt, k half kk) -> block mt*2+kk, lane order
@@ -362,7 +356,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const float* __restrict__ w2, float b2, float* __restrict__ scores, int32_t T, int32_t d,
     int32_t h) {
   constexpr int TM = 64;
-  constexpr int DEPTH = TG_GATE_DEPTH;
+  constexpr int DEPTH = kDepth;
   constexpr int R = DEPTH + 1;                 // ring length
   constexpr int XPW = 8 / NW;                  // residual blocks each wave loads per stage
   constexpr int PER_STAGE = XPW + 2 * NTW;     // vector-memory instructions per wave per stage
@@ -767,7 +761,7 @@ tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int
   if (rms_weight != nullptr && d > 16384)
     return fail(TG_ERR_UNSUPPORTED,
                 "%s: bf16 path with an RMSNorm weight needs d <= 16384 (LDS-staged)", fn);
-  if (static_cast<int64_t>(TG_GATE_TM) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
+  if (static_cast<int64_t>(kTM) * resid_row_stride * 2 > kMaxTokens || h * d * 2 > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED,
                 "%s: bf16 path addresses a 64-row tile and W1 with 31-bit offsets", fn);
   if (!aligned(resid, 16) || !aligned(w1, 16) || (resid_row_stride % 8) != 0)
@@ -785,7 +779,7 @@ tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int
     return check_launch(fn);
   }
   const bool g = rms_weight != nullptr;
-  constexpr int TM = TG_GATE_TM;
+  constexpr int TM = kTM;
   const dim3 grid(static_cast<uint32_t>((T + TM - 1) / TM));
   switch (h / 64) {
     case 1: launch_bf16<TM, 1>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;

@@ -2,6 +2,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+
 #include "tg_common.hpp"
 
 namespace {
@@ -19,6 +21,20 @@ tg_status fail(tg_status s, const char* fmt, ...) {
 }
 
 void clear_error() { g_last_error[0] = '\0'; }
+
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus[kMaxDevices];   // 0: not read yet
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 tg_status check_launch(const char* what) {
   hipError_t e = hipGetLastError();

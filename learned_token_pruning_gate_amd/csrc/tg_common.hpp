@@ -27,6 +27,10 @@ inline bool aligned(const void* p, uintptr_t a) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Compute units of the current device, read from the runtime once per
+// device and cached (256 on MI355X); 256 if the query fails.
+int device_cu_count();
+
 constexpr int64_t kMaxTokens = 2147483647LL;  // token counts fit in int32
 
 // ---- device side ---------------------------------------------------------

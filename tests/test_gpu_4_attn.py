@@ -190,28 +190,51 @@ def test_attn_deterministic():
 
 
 # ---- full sizes --------------------------------------------------------------
-def test_attn_bf16_t16k_full():
-    """N = 2512 kept tokens, 16/8 heads, D = 128: every output row."""
+@pytest.mark.parametrize("entry", ["unsplit", "split"])
+def test_attn_bf16_t16k_full(entry):
+    """N = 2512 kept tokens, 16/8 heads, D = 128, causal: every output row.
+    "split" is the launch the chain and the benchmark time
+    (tg_bias_attn_fwd_ws with the queried workspace); gpu_split fails if the
+    cost model stops splitting this shape."""
     w = workloads.get("t16k")
     _, a = workloads.generate(w)
     rng = np.random.default_rng(90)
     s = rng.standard_normal(w.n_kept).astype(np.float32)
-    o, lse = gpu(a.q, a.k, a.v, s, a.gain, None, "bf16")
+    if entry == "split":
+        o, lse = gpu_split(a.q, a.k, a.v, s, a.gain, None)
+    else:
+        o, lse = gpu(a.q, a.k, a.v, s, a.gain, None, "bf16")
     ro, rl = ref(a.q, a.k, a.v, s, a.gain, None, "bf16")
-    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_t16k_full")
-    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_bf16_t16k_full_lse")
+    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_t16k_full_" + entry)
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_bf16_t16k_full_lse_" + entry)
+
+
+def dense_rows(N, block=128, seed=91):
+    """Rows checked on the dense 32k prompt: the first and last row of every
+    block of `block` queries (a workgroup's query block of the large-grid
+    launch), the tail, and a random sample."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, N, block)
+    return np.unique(np.concatenate([starts, np.minimum(starts + block - 1, N - 1),
+                                     [1, 63, 64, 65], np.arange(N - 40, N),
+                                     rng.choice(N, size=60, replace=False)]))
 
 
 def test_attn_bf16_dense_sampled_rows():
-    """N = 32768 (every token kept): sampled rows, weighted to the long ones."""
+    """N = 32768 (every token kept): the first and last row of each 128-query
+    block plus a random sample, with the workload's drawn key scores and its
+    per-query scale array, through tg_bias_attn_fwd_ws as the benchmark
+    calls it (no workspace: the shape fills the chip unsplit)."""
     w = workloads.get("t32k-dense")
     _, a = workloads.generate(w)
     N = w.n_kept
+    assert tg.tg_bias_attn_workspace_size(N, w.Hq, w.Hkv, w.D) == 0
     c = workloads.q_scale_pos_rank(np.arange(N))
-    o, lse = gpu(a.q, a.k, a.v, a.drawn_scores, a.gain, c, "bf16")
-    rng = np.random.default_rng(91)
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 65, 127, 128], np.arange(N - 40, N),
-                                     rng.choice(N, size=60, replace=False)]))
+    o, lse = tg.tg_bias_attn_fwd_ws(to_dev(a.q, "bf16"), to_dev(a.k, "bf16"),
+                                    to_dev(a.v, "bf16"), to_dev(a.drawn_scores),
+                                    to_dev(a.gain), None, to_dev(c))
+    torch.cuda.synchronize()
+    rows = dense_rows(N)
     ro, rl = ref(a.q, a.k, a.v, a.drawn_scores, a.gain, c, "bf16", rows=rows)
     assert_close_abs(as_f64(o)[rows], ro, BF16_ABS, "attn_bf16_dense_sampled")
     assert_close_abs(lse.cpu().numpy()[:, rows], rl, LSE_ABS_BF16, "attn_bf16_dense_lse")
@@ -223,6 +246,7 @@ SPLIT_SHAPES = [  # N, Hq, Hkv, D, causal: each takes the split (3 to 7 chunks p
     (1000, 4, 4, 64, True), (1000, 4, 4, 64, False),       # 1 head per KV head
     (1700, 6, 2, 64, True), (1700, 6, 2, 64, False),       # 3 heads per KV head
     (2512, 8, 4, 128, True), (2512, 16, 8, 128, False),    # the 16k prompt's kept set size
+    (2512, 16, 8, 128, True),                              # ... at its heads: the timed launch
     (1500, 16, 8, 128, True),
     (1800, 12, 4, 64, True),
     (2999, 8, 8, 128, True),                               # ragged last query block
@@ -306,3 +330,26 @@ def test_attn_bf16_t16k_full_split():
     ro, rl = ref(a.q, a.k, a.v, s, a.gain, None, "bf16")
     assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_bf16_t16k_full_split")
     assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_bf16_t16k_full_split_lse")
+
+
+@pytest.mark.parametrize("entry", ["unsplit", "split"])
+def test_attn_small_q_scale_deletes_keys(entry):
+    """A -inf score deletes its key at any per-query scale, including ones
+    far below 1 (here 0.1 and 0.01): rows whose visible keys are all deleted
+    give O = 0 and lse = -inf, and the other rows match the oracle on the
+    keys that remain."""
+    rng = np.random.default_rng(93)
+    N, Hq, Hkv, D = 2512, 8, 4, 128
+    q, k, v, s, g, _ = make(rng, N, Hq, Hkv, D, "bf16")
+    c = np.where(np.arange(N) % 2 == 0, 0.1, 0.01).astype(np.float32)
+    s[:300] = -np.inf
+    if entry == "split":
+        o, lse = gpu_split(q, k, v, s, g, c)
+    else:
+        o, lse = gpu(q, k, v, s, g, c, "bf16")
+    assert torch.all(o[:300].float() == 0)
+    assert torch.all(torch.isneginf(lse[:, :300]))
+    ro, rl = ref(q[300:], k[300:], v[300:], s[300:], g, c[300:], "bf16")
+    assert_close_abs(as_f64(o)[300:], ro, BF16_ABS, "attn_small_qscale_" + entry)
+    assert_close_abs(lse.cpu().numpy()[:, 300:], rl, LSE_ABS_BF16,
+                     "attn_small_qscale_lse_" + entry)

@@ -1,20 +1,19 @@
 """End-to-end: gate -> select -> gather -> bias attention on the GPU, each
-stage checked against the oracle on every workload.
+stage checked against the oracle on every workload (tests/chain_oracle.py
+states the rules and tolerances).
 
-Selection rule end to end: the GPU kept set must equal the oracle's selection
-on the GPU's own fp32 scores exactly; where the oracle's fp64 scores are
-available for every token, it may differ from the oracle's selection on them
-only at tokens whose oracle score lies within the score tolerance of the
-threshold."""
+The attention runs through tg_bias_attn_fwd_ws with the workspace that
+tg_bias_attn_workspace_size gives for the shape (none when it runs unsplit),
+which is the launch that the captured chain and the benchmark time; the
+"unsplit" cases take the same pass through tg_bias_attn_fwd."""
 import numpy as np
 import pytest
 import torch
 
 import learned_token_pruning_gate_amd as tg
-import oracle
 import workloads
-from gpu_util import (BF16_ABS, F32_REL, as_f64, assert_close_abs, assert_close_f32, report,
-                      to_dev)
+from chain_oracle import check_chain
+from gpu_util import as_f64, bf16_bits, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +21,7 @@ ALL = ["tiny", "tiny-K32", "t16k", "t32k-K100", "t32k-K500", "t32k-K2000", "t32k
        "t128k", "t32k-dense", "t16k-d256"]
 
 
-def run_chain(w, g, a, planted=None):
+def run_chain(w, g, a, planted=None, entry="ws"):
     dt = w.dtype
     resid = to_dev(g.resid, dt)
     prunable = to_dev(g.prunable)
@@ -35,96 +34,38 @@ def run_chain(w, g, a, planted=None):
     N = w.n_kept
     resid_kept, pos_kept, score_kept = tg.tg_compact_gather(resid, scores, kept, N)
     key_score = to_dev(a.drawn_scores) if w.drawn_key_scores else score_kept
-    q_scale = None
-    if w.q_scale_recipe == "pos_rank":
-        q_scale = to_dev(workloads.q_scale_pos_rank(np.arange(N)))  # replaced below
     torch.cuda.synchronize()
     pos_host = pos_kept.cpu().numpy()
+    q_scale = None
     if w.q_scale_recipe == "pos_rank":
         q_scale = to_dev(workloads.q_scale_pos_rank(pos_host))
-    out, lse = tg.tg_bias_attn_fwd(to_dev(a.q, dt), to_dev(a.k, dt), to_dev(a.v, dt), key_score,
-                                   to_dev(a.gain), q_scale)
+    q, k, v, gain = to_dev(a.q, dt), to_dev(a.k, dt), to_dev(a.v, dt), to_dev(a.gain)
+    split = False
+    if entry == "ws":
+        nb = tg.tg_bias_attn_workspace_size(N, w.Hq, w.Hkv, w.D, True, q.dtype)
+        ws = torch.empty(nb, dtype=torch.uint8, device=q.device) if nb else None
+        split = ws is not None
+        out, lse = tg.tg_bias_attn_fwd_ws(q, k, v, key_score, gain, ws, q_scale)
+    else:
+        out, lse = tg.tg_bias_attn_fwd(q, k, v, key_score, gain, q_scale)
     torch.cuda.synchronize()
+    rk = bf16_bits(resid_kept) if dt == "bf16" else resid_kept.cpu().numpy()
     return dict(scores=scores.cpu().numpy(), n_kept=int(n_kept.item()),
-                kept=kept.cpu().numpy()[:N], resid_kept=resid_kept, pos=pos_host,
-                score_kept=score_kept.cpu().numpy(),
-                key_score=key_score.cpu().numpy(),
+                kept=kept.cpu().numpy()[:N], resid_kept=rk, pos=pos_host,
+                score_kept=score_kept.cpu().numpy(), key_score=key_score.cpu().numpy(),
                 q_scale=None if q_scale is None else q_scale.cpu().numpy(),
-                out=out, lse=lse.cpu().numpy())
+                out=as_f64(out), lse=lse.cpu().numpy(), split=split)
 
 
-@pytest.mark.parametrize("name", ALL)
-def test_chain(name):
+CASES = [(n, "ws") for n in ALL] + [("t16k", "unsplit"), ("t16k-d256", "unsplit")]
+
+
+@pytest.mark.parametrize("name,entry", CASES)
+def test_chain(name, entry):
     w = workloads.get(name)
     g, a = workloads.generate(w)
     planted = workloads.planted_block(w, g) if w.planted_block else None
-    r = run_chain(w, g, a, planted)
-    N = w.n_kept
-
-    # gate: every row for the smaller workloads, sampled rows beyond
-    full_gate = w.T <= 16384
-    if full_gate:
-        rows = np.arange(w.T)
-    else:
-        rng = np.random.default_rng(w.seed + 1)
-        rows = np.unique(np.concatenate([np.arange(512), np.arange(w.T - 512, w.T),
-                                         rng.choice(w.T, 2000, replace=False)]))
-    ref_s = oracle.gate_score(workloads.as_f64(g.resid[rows], w.dtype), g.prunable[rows],
-                              workloads.as_f64(g.w1, w.dtype), g.w2, b2=g.b2, gamma=g.gamma,
-                              b1=g.b1, eps=g.eps)
-    got_s = r["scores"].astype(np.float64)
-    if planted is not None:
-        p0, vals = planted
-        ref_s = ref_s.copy()
-        sel = (rows >= p0) & (rows < p0 + 64)
-        ref_s[sel] = vals[rows[sel] - p0]
-    if w.dtype == "f32":
-        assert_close_f32(got_s[rows], ref_s, "chain_gate_" + name)
-    else:
-        assert_close_abs(got_s[rows], ref_s, BF16_ABS, "chain_gate_" + name)
-
-    # select: exact on the GPU's own scores
-    ref_kept = oracle.topk_select(r["scores"], g.prunable, w.K)
-    assert r["n_kept"] == N == len(ref_kept)
-    assert np.array_equal(r["kept"], ref_kept)
-    if full_gate:   # against the oracle's own scores: differences only near the threshold
-        ref_kept2 = oracle.topk_select(ref_s.astype(np.float32), g.prunable, w.K)
-        diff = np.setxor1d(ref_kept, ref_kept2)
-        if diff.size:
-            tol = F32_REL if w.dtype == "f32" else BF16_ABS
-            pr = np.nonzero(g.prunable)[0]
-            thr = np.sort(ref_s[pr])[::-1][min(w.K, len(pr)) - 1]
-            assert np.all(np.abs(ref_s[diff] - thr) <= 2 * tol), "selection differs far from threshold"
-        report("chain_select_" + name, N=N, differs_from_fp64_selection=int(diff.size))
-    if planted is not None:
-        p0, _ = planted
-        assert set(range(p0, p0 + 64)) <= set(r["kept"].tolist())
-
-    # gather: bit-exact
-    rows_k = r["resid_kept"]
-    got_rows = rows_k.view(torch.int16).cpu().numpy().view(np.uint16) if w.dtype == "bf16" \
-        else rows_k.cpu().numpy()
-    assert got_rows.tobytes() == g.resid[r["kept"]].tobytes()
-    assert np.array_equal(r["pos"], r["kept"])
-    assert r["score_kept"].tobytes() == r["scores"][r["kept"]].tobytes()
-
-    # attention on the GPU's kept scores (or the drawn ones), all rows or a sample
-    if N <= 2600:
-        arows = None
-    else:
-        rng = np.random.default_rng(w.seed + 2)
-        arows = np.unique(np.concatenate([np.arange(64), np.arange(N - 32, N),
-                                          rng.choice(N, 48, replace=False)]))
-    ro, rl = oracle.bias_attn(workloads.as_f64(a.q, w.dtype), workloads.as_f64(a.k, w.dtype),
-                              workloads.as_f64(a.v, w.dtype), r["key_score"], a.gain,
-                              q_scale=r["q_scale"], rows=arows)
-    go = as_f64(r["out"])
-    gl = r["lse"]
-    if arows is not None:
-        go, gl = go[arows], gl[:, arows]
-    if w.dtype == "f32":
-        assert_close_f32(go, ro, "chain_attn_" + name)
-        assert_close_f32(gl, rl, "chain_lse_" + name)
-    else:
-        assert_close_abs(go, ro, BF16_ABS, "chain_attn_" + name)
-        assert_close_abs(gl, rl, BF16_ABS, "chain_lse_" + name)
+    r = run_chain(w, g, a, planted, entry)
+    if name in ("t16k", "t16k-d256") and entry == "ws":
+        assert r["split"], "the 16k prompt's attention is expected to take the split"
+    check_chain(w, g.resid, g.prunable, g, a, r, "chain_%s_%s" % (name, entry), planted)

@@ -1,22 +1,26 @@
 """The four calls captured as one HIP graph (tg_chain_create / launch): every
 replay must reproduce the eager chain bit for bit, also after the inputs are
-refilled in place and with eager work and synchronisation between replays.
-(TokenGate pages: ai.info summary "Key Contributions" item 4, the graph-
-captured serving recipe.)"""
+refilled in place and with eager work and synchronisation between replays,
+and the replays' outputs, before and after the refill, must match the oracle
+(tests/chain_oracle.py).  (TokenGate pages: ai.info summary "Key
+Contributions" item 4, the graph-captured serving recipe.)"""
 import numpy as np
 import pytest
 import torch
 
 import learned_token_pruning_gate_amd as tg
+import oracle
 import workloads
+from chain_oracle import check_chain
 from dataclasses import replace
-from gpu_util import report, to_dev
+from gpu_util import as_f64, bf16_bits, report, to_dev
 
 pytestmark = pytest.mark.gpu
 
 
-def make_case(w, packed, kv_layers=0, split=False):
-    g, a = workloads.generate(w)
+def make_case(w, packed, kv_layers=0, split=False, g=None, a=None):
+    if g is None:
+        g, a = workloads.generate(w)
     dt = w.dtype
     c = dict(resid=to_dev(g.resid, dt), prunable=to_dev(g.prunable), w2=to_dev(g.w2),
              b1=to_dev(g.b1), q=to_dev(a.q, dt), k=to_dev(a.k, dt), v=to_dev(a.v, dt),
@@ -98,8 +102,23 @@ def same(c, ref, what):
                            b.view(torch.uint8) if b.dtype == torch.bfloat16 else b), (what, n)
 
 
+def host(t, dt):
+    return bf16_bits(t) if dt == "bf16" else t.cpu().numpy()
+
+
+def replay_outputs(c, w):
+    """The chain's outputs in the form check_chain takes."""
+    N = w.n_kept
+    return dict(scores=c["scores"].cpu().numpy(), n_kept=int(c["n_kept"].item()),
+                kept=c["kept_idx"].cpu().numpy()[:N], resid_kept=host(c["resid_kept"], w.dtype),
+                pos=c["pos_kept"].cpu().numpy(), score_kept=c["score_kept"].cpu().numpy(),
+                key_score=c["score_kept"].cpu().numpy(), q_scale=None, out=as_f64(c["out"]),
+                lse=c["lse"].cpu().numpy())
+
+
 CASES = [
     ("tiny", False, 0, False),
+    ("t16k", True, 0, True),     # the benchmark's chain: packed W1, split attention
     ("t16k", True, 0, False),
     ("t16k", False, 0, False),
     ("t16k", True, 2, False),    # with the lower layers' KV gather on a forked stream
@@ -115,7 +134,8 @@ def test_graph_replays_match_eager(name, packed, kv_layers, split):
                     p_lo=100, p_hi=39900, K=700)
     else:
         w = workloads.get(name)
-    c = make_case(w, packed, kv_layers, split)
+    g, a = workloads.generate(w)
+    c = make_case(w, packed, kv_layers, split, g, a)
     ref = eager(c, w, packed)
     kv = {n: c[n] for n in ("kv_k_cache", "kv_v_cache", "kv_k_kept", "kv_v_kept") if n in c}
     chain = tg.tg_chain_create(
@@ -131,6 +151,14 @@ def test_graph_replays_match_eager(name, packed, kv_layers, split):
         chain.launch()
         torch.cuda.synchronize()
         same(c, ref, "%s replay %d" % (name, rep))
+        if rep == 0:
+            check_chain(w, g.resid, g.prunable, g, a, replay_outputs(c, w),
+                        "graph_%s_p%d_kv%d_s%d" % (name, packed, kv_layers, split))
+            kept_host = c["kept_idx"].cpu().numpy()[:w.n_kept]
+            for src, dst in (("kv_k_cache", "kv_k_kept"), ("kv_v_cache", "kv_v_kept")):
+                if src in c:   # the lower layers' KV gather, bit-exact
+                    want = oracle.kv_gather(host(c[src], w.dtype), kept_host)
+                    assert host(c[dst], w.dtype).tobytes() == want.tobytes(), (name, dst)
     # refill the inputs in place: the graph reads the new values
     gen = torch.Generator(device=c["resid"].device).manual_seed(5)
     c["resid"].copy_(torch.randn(c["resid"].shape, generator=gen, device=c["resid"].device)
@@ -143,6 +171,9 @@ def test_graph_replays_match_eager(name, packed, kv_layers, split):
     chain.launch()                     # two replays in a row on one stream
     torch.cuda.synchronize()
     same(c, ref2, name + " refilled")
+    check_chain(w, host(c["resid"], w.dtype), g.prunable, g, a, replay_outputs(c, w),
+                "graph_%s_p%d_kv%d_s%d_refilled" % (name, packed, kv_layers, split),
+                q=host(c["q"], w.dtype))
     chain.close()
     report("graph_chain_" + name, packed=packed, kv_layers=kv_layers, split=split, replays=5,
            bit_exact=True)
