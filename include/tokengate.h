@@ -176,6 +176,24 @@ tg_status tg_topk_select(int64_t T, const float* scores,
                          size_t workspace_bytes, void* stream);
 
 /* --------------------------------------------------------------------------
+ * tg_topk_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same operation, arguments, kernels
+ * and results as tg_topk_select (bit for bit); its scratch is instead a
+ * static device array of 64 KiB in the library, one copy per GPU, held until
+ * the process ends, which covers every T up to 2^31 - 1 (the workspace of
+ * the largest T is 53.5 KiB; a T whose workspace exceeded the array would
+ * return TG_ERR_UNSUPPORTED).  The first call on a device looks the array up
+ * and enqueues one kernel on `stream` that clears it; no call allocates.
+ * Every call on one GPU shares that GPU's array, so calls that can overlap
+ * on one GPU (unordered streams, threads) race: order them on one stream.
+ * ------------------------------------------------------------------------ */
+tg_status tg_topk_select_noalloc(int64_t T, const float* scores,
+                                 const uint8_t* prunable, int64_t K,
+                                 int32_t* kept_idx, int64_t kept_capacity,
+                                 int32_t* n_kept, void* stream);
+
+/* --------------------------------------------------------------------------
  * [a4] Gather into kept order.  Pages: ai.info summary "Key Contributions"
  * item 1 and the README mirror "How it works": layers above the gate
  * process, and keep KV entries for, only the kept tokens.

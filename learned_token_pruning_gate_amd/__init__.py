@@ -13,6 +13,8 @@ Entry points (same names as the C ABI):
                           -- the same scorer with W1 packed once, at weight
                              load, into the MFMA fragment order
 * ``tg_topk_workspace_size`` / ``tg_topk_select`` -- top-K + compaction
+* ``tg_topk_select_noalloc`` -- the same with the library's static scratch
+                          (for callers that cannot allocate device memory)
 * ``tg_compact_gather``   -- gather of rows, positions and scores
 * ``tg_bias_attn_fwd``    -- causal GQA attention with the gate bias
 * ``tg_bias_attn_workspace_size`` / ``tg_bias_attn_fwd_ws`` -- the same with
@@ -34,7 +36,8 @@ __all__ = [
     "TokenGateError", "lib_path", "load", "kept_count",
     "tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
     "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-    "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd", "tg_bias_attn_workspace_size",
+    "tg_topk_select", "tg_topk_select_noalloc", "tg_compact_gather", "tg_bias_attn_fwd",
+    "tg_bias_attn_workspace_size",
     "tg_bias_attn_fwd_ws", "tg_bias_attn_bwd_workspace_size", "tg_bias_attn_bwd",
     "tg_kv_gather", "tg_chain_create", "TgChain",
     "TG_OK", "TG_ERR_INVALID_ARGUMENT", "TG_ERR_UNSUPPORTED", "TG_ERR_WORKSPACE",
@@ -49,7 +52,7 @@ TG_DTYPE_F32, TG_DTYPE_BF16 = 0, 1
 
 EXPORTED = ("tg_status_str", "tg_last_error", "tg_gate_score", "tg_gate_w1_packed_bytes",
             "tg_gate_pack_w1", "tg_gate_score_packed", "tg_topk_workspace_size",
-            "tg_topk_select", "tg_compact_gather", "tg_bias_attn_fwd",
+            "tg_topk_select", "tg_topk_select_noalloc", "tg_compact_gather", "tg_bias_attn_fwd",
             "tg_bias_attn_workspace_size", "tg_bias_attn_fwd_ws",
             "tg_bias_attn_bwd_workspace_size", "tg_bias_attn_bwd", "tg_kv_gather",
             "tg_chain_create",
@@ -111,6 +114,8 @@ def load():
     lib.tg_topk_workspace_size.restype = ctypes.c_size_t
     lib.tg_topk_select.argtypes = [I64, P, P, I64, P, I64, P, P, ctypes.c_size_t, P]
     lib.tg_topk_select.restype = I
+    lib.tg_topk_select_noalloc.argtypes = [I64, P, P, I64, P, I64, P, P]
+    lib.tg_topk_select_noalloc.restype = I
     lib.tg_compact_gather.argtypes = [I, I64, I64, I64, P, I64, P, P, P, I64, P, P, P]
     lib.tg_compact_gather.restype = I
     lib.tg_bias_attn_fwd.argtypes = [I, I64, I64, I64, I64, P, P, P, P, P, P, F, I, P, P, P]
@@ -391,6 +396,26 @@ def tg_topk_select(scores, prunable, K, kept_idx=None, n_kept=None, workspace=No
                             kept_idx.numel(), _ptr(n_kept), _ptr(workspace),
                             workspace.numel(), _stream(stream))
     _check(st, "tg_topk_select")
+    return kept_idx, n_kept
+
+
+def tg_topk_select_noalloc(scores, prunable, K, kept_idx=None, n_kept=None, stream=None):
+    """tg_topk_select with the library's static scratch (no workspace
+    argument): (kept_idx, n_kept) as tg_topk_select returns them."""
+    lib = load()
+    _dev(scores, "scores", torch.float32)
+    _dev(prunable, "prunable", torch.uint8)
+    T = scores.shape[0]
+    dev = scores.device
+    if kept_idx is None:
+        kept_idx = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    _dev(kept_idx, "kept_idx", torch.int32)
+    if n_kept is None:
+        n_kept = torch.empty(1, dtype=torch.int32, device=dev)
+    _dev(n_kept, "n_kept", torch.int32)
+    st = lib.tg_topk_select_noalloc(T, _ptr(scores), _ptr(prunable), int(K), _ptr(kept_idx),
+                                    kept_idx.numel(), _ptr(n_kept), _stream(stream))
+    _check(st, "tg_topk_select_noalloc")
     return kept_idx, n_kept
 
 

@@ -25,7 +25,17 @@
 // look-back descriptors.  It must start all-zero; the last workgroup of each
 // pass clears what that pass used, so every call ends with it all-zero.  The
 // first histogram pass also resets the compaction's ticket and descriptors.
+#include <mutex>
+
 #include "tg_common.hpp"
+
+// Scratch of tg_topk_select_noalloc: the select workspace as a file-scope
+// device array, one copy on each GPU the library runs on, held until the
+// process ends.  Host code never passes this name to a kernel (on the host
+// it is only a stand-in for the symbol); it uses the device address that
+// hipGetSymbolAddress returns for the current device.  The workspace of the
+// largest T (4096 look-back descriptors) is 53.5 KiB; 64 KiB covers every T.
+static __device__ __align__(256) uint8_t scratch[64 * 1024];
 
 namespace tg {
 namespace {
@@ -615,39 +625,73 @@ extern "C" size_t tg_topk_workspace_size(int64_t T) {
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
-extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_t* prunable,
-                                    int64_t K, int32_t* kept_idx, int64_t kept_capacity,
-                                    int32_t* n_kept, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
-  using namespace tg;
+namespace tg {
+namespace {
+
+__global__ void zero_bytes_kernel(uint8_t* __restrict__ p, int32_t n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+// Device address of `scratch` on the current device, looked up (and the
+// array cleared on `s`) on the first call on each device.
+tg_status static_scratch(hipStream_t s, uint8_t** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(TG_ERR_LAUNCH, "tg_topk_select_noalloc: no usable current device (%s)",
+                hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TG_ERR_LAUNCH, "tg_topk_select_noalloc: hipGetSymbolAddress failed: %s",
+                  hipGetErrorString(e));
+    // the selection needs an all-zero workspace: clear it once, with a kernel
+    zero_bytes_kernel<<<dim3(sizeof(scratch) / 256), dim3(256), 0, s>>>(
+        static_cast<uint8_t*>(p), static_cast<int32_t>(sizeof(scratch)));
+    const tg_status st = check_launch("tg_topk_select_noalloc");
+    if (st != TG_OK) return st;
+    ptr[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(ptr[dev]);
+  return TG_OK;
+}
+
+// Host-side checks of tg_topk_select's arguments (all but the workspace).
+tg_status select_check(const char* fn, int64_t T, const float* scores, const uint8_t* prunable,
+                       int64_t K, const int32_t* kept_idx, int64_t kept_capacity,
+                       const int32_t* n_kept) {
   if (T < 0 || T > kMaxTokens)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: need 0 <= T <= 2^31-1 (T=%lld)",
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: need 0 <= T <= 2^31-1 (T=%lld)", fn,
                 (long long)T);
   if (K < 0)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: K must be >= 0 (K=%lld)",
-                (long long)K);
-  if (kept_capacity < 0)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: kept_capacity < 0");
-  if (n_kept == nullptr)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: n_kept is NULL");
-  hipStream_t s = as_stream(stream);
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: K must be >= 0 (K=%lld)", fn, (long long)K);
+  if (kept_capacity < 0) return fail(TG_ERR_INVALID_ARGUMENT, "%s: kept_capacity < 0", fn);
+  if (n_kept == nullptr) return fail(TG_ERR_INVALID_ARGUMENT, "%s: n_kept is NULL", fn);
+  if (T == 0) return TG_OK;
+  if (scores == nullptr || prunable == nullptr)
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: scores/prunable is NULL", fn);
+  if (kept_idx == nullptr && kept_capacity > 0)
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: kept_idx is NULL", fn);
+  if (!aligned(scores, 4) || !aligned(kept_idx, 4) || !aligned(n_kept, 4))
+    return fail(TG_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", fn);
+  return TG_OK;
+}
+
+// The launches of a checked call; ws holds at least tg_topk_workspace_size(T)
+// bytes, 256-byte aligned, all zero.
+tg_status select_launch(const char* fn, int64_t T, const float* scores,
+                        const uint8_t* prunable, int64_t K, int32_t* kept_idx,
+                        int64_t kept_capacity, int32_t* n_kept, uint8_t* ws, hipStream_t s) {
   if (T == 0) {
     write_zero_kernel<<<1, 1, 0, s>>>(n_kept);
-    return check_launch("tg_topk_select");
+    return check_launch(fn);
   }
-  if (scores == nullptr || prunable == nullptr)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: scores/prunable is NULL");
-  if (kept_idx == nullptr && kept_capacity > 0)
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: kept_idx is NULL");
-  if (!aligned(scores, 4) || !aligned(kept_idx, 4) || !aligned(n_kept, 4))
-    return fail(TG_ERR_INVALID_ARGUMENT, "tg_topk_select: misaligned pointer");
-  const size_t need_bytes = tg_topk_workspace_size(T);
-  if (workspace == nullptr || workspace_bytes < need_bytes)
-    return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace needs %zu bytes, got %zu",
-                need_bytes, workspace == nullptr ? (size_t)0 : workspace_bytes);
-  if (!aligned(workspace, 256))
-    return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace must be 256-byte aligned");
-
   const uint32_t Kc = static_cast<uint32_t>(K < T ? K : T);
   if (T <= kLdsTokens && aligned(prunable, 16)) {
     if (T <= kLdsTokens / 2)
@@ -656,11 +700,10 @@ extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_
     else
       select_one_wg_kernel<kLdsTokens><<<dim3(1), dim3(kOneThreads), 0, s>>>(
           scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept);
-    return check_launch("tg_topk_select");
+    return check_launch(fn);
   }
   int64_t per_block = 0;
   const int64_t G = blocks_for(T, &per_block);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int32_t T32 = static_cast<int32_t>(T);
   radix_hist_kernel<0><<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block,
                                                            Kc, static_cast<uint32_t>(G), ws);
@@ -670,5 +713,48 @@ extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_
                                                            Kc, static_cast<uint32_t>(G), ws);
   compact_kernel<<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block, ws,
                                                      kept_idx, kept_capacity, n_kept);
-  return check_launch("tg_topk_select");
+  return check_launch(fn);
+}
+
+}  // namespace
+}  // namespace tg
+
+extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_t* prunable,
+                                    int64_t K, int32_t* kept_idx, int64_t kept_capacity,
+                                    int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  using namespace tg;
+  tg_status st = select_check("tg_topk_select", T, scores, prunable, K, kept_idx,
+                              kept_capacity, n_kept);
+  if (st != TG_OK) return st;
+  if (T > 0) {
+    const size_t need_bytes = tg_topk_workspace_size(T);
+    if (workspace == nullptr || workspace_bytes < need_bytes)
+      return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace needs %zu bytes, got %zu",
+                  need_bytes, workspace == nullptr ? (size_t)0 : workspace_bytes);
+    if (!aligned(workspace, 256))
+      return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace must be 256-byte aligned");
+  }
+  return select_launch("tg_topk_select", T, scores, prunable, K, kept_idx, kept_capacity,
+                       n_kept, static_cast<uint8_t*>(workspace), as_stream(stream));
+}
+
+extern "C" tg_status tg_topk_select_noalloc(int64_t T, const float* scores,
+                                            const uint8_t* prunable, int64_t K,
+                                            int32_t* kept_idx, int64_t kept_capacity,
+                                            int32_t* n_kept, void* stream) {
+  using namespace tg;
+  const char* fn = "tg_topk_select_noalloc";
+  tg_status st = select_check(fn, T, scores, prunable, K, kept_idx, kept_capacity, n_kept);
+  if (st != TG_OK) return st;
+  const size_t need = tg_topk_workspace_size(T);
+  if (need > sizeof(scratch))
+    return fail(TG_ERR_UNSUPPORTED,
+                "%s: T=%lld needs %zu bytes of scratch, the static array holds %zu", fn,
+                (long long)T, need, sizeof(scratch));
+  hipStream_t s = as_stream(stream);
+  uint8_t* ws = nullptr;
+  st = static_scratch(s, &ws);
+  if (st != TG_OK) return st;
+  return select_launch(fn, T, scores, prunable, K, kept_idx, kept_capacity, n_kept, ws, s);
 }

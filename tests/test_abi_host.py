@@ -142,6 +142,25 @@ def test_select_validation(lib):
     assert "workspace" in lib.tg_last_error().decode()
 
 
+def test_select_noalloc_validation(lib):
+    """The allocation-free variant checks its arguments as tg_topk_select
+    does, before it touches a device (no workspace argument to check)."""
+    def sel(T=100, scores=FAKE, prunable=FAKE, K=10, kept=FAKE, cap=100, n_kept=FAKE):
+        return lib.tg_topk_select_noalloc(T, scores, prunable, K, kept, cap, n_kept, None)
+    assert sel(T=-1) == INVAL
+    assert sel(T=2**31) == INVAL
+    assert sel(K=-1) == INVAL
+    assert sel(cap=-1) == INVAL
+    assert sel(n_kept=None) == INVAL
+    assert sel(scores=None) == INVAL
+    assert sel(prunable=None) == INVAL
+    assert sel(kept=None) == INVAL
+    assert sel(scores=FAKE_ODD) == INVAL
+    assert "tg_topk_select_noalloc" in lib.tg_last_error().decode()
+    # the static scratch (64 KiB) covers the workspace of every valid T
+    assert lib.tg_topk_workspace_size(2**31 - 1) <= 64 * 1024
+
+
 def _gather(lib, dt=BF16, T=100, N=10, d=64, resid=FAKE, sstride=64, scores=FAKE,
             idx=FAKE, out=FAKE, dstride=64, pos=FAKE, sk=FAKE):
     return lib.tg_compact_gather(dt, T, N, d, resid, sstride, scores, idx, out, dstride, pos,
