@@ -98,6 +98,31 @@ def test_attn_bf16_shapes(N, Hq, Hkv, D, causal):
     assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, tag + "_lse")
 
 
+# Grids of more than 1024 four-wave workgroups take the large-grid launch
+# (8-wave workgroups whose two wave groups alternate between matrix products
+# and softmax): 1, 2 and 4 query heads per KV head, head dims 64 and 128,
+# ragged last query blocks.  Rows checked: the first and last of every 64-row
+# block plus a random sample.
+LARGE_SHAPES = [  # N, Hq, Hkv, D
+    (4500, 32, 16, 128), (9000, 16, 4, 128), (3001, 64, 64, 128), (4500, 32, 8, 64),
+    (8191, 16, 8, 128),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,D", LARGE_SHAPES)
+@pytest.mark.parametrize("causal", [True, False])
+def test_attn_bf16_large_grid(N, Hq, Hkv, D, causal):
+    rng = np.random.default_rng(N * 13 + Hq + D + causal)
+    q, k, v, s, g, c = make(rng, N, Hq, Hkv, D, "bf16")
+    s[rng.choice(N, 20, replace=False)] = -np.inf      # some deleted keys
+    o, lse = gpu(q, k, v, s, g, c, "bf16", causal=causal)
+    rows = dense_rows(N, block=64, seed=N)
+    ro, rl = ref(q, k, v, s, g, c, "bf16", causal=causal, rows=rows)
+    tag = "attn_large_N%d_H%d_%d_D%d_c%d" % (N, Hq, Hkv, D, causal)
+    assert_close_abs(as_f64(o)[rows], ro, BF16_ABS, tag)
+    assert_close_abs(lse.cpu().numpy()[:, rows], rl, LSE_ABS_BF16, tag + "_lse")
+
+
 @pytest.mark.parametrize("bias,qscale", [(False, False), (True, False), (False, True)])
 def test_attn_bf16_optional_inputs(bias, qscale):
     rng = np.random.default_rng(77)
