@@ -372,25 +372,39 @@ tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv
 /* --------------------------------------------------------------------------
  * The four calls captured once as a HIP graph and replayed.  Pages: ai.info
  * summary "Key Contributions" item 4 (the serving recipe captures the pruned
- * forward pass as a graph, so the short kernels of a small budget are not
- * paced by launches).  The four calls above enqueue only kernels and never
- * synchronise, so they are capturable as they stand.
+ * forward pass as a graph per padded length, so the short kernels of a small
+ * budget are not paced by launches).  The four calls above enqueue only
+ * kernels and never synchronise, so they are capturable as they stand.
  *
  * tg_chain_desc holds the arguments of the four calls, field for field as
  * documented above (w1_packed selects tg_gate_score_packed; attn_key_score
  * is the attention's key_score, normally score_kept; attn_workspace, if not
- * NULL, selects tg_bias_attn_fwd_ws; the kv_ fields, if
- * kv_L > 0, add tg_kv_gather with the desc's T, N, Hkv, D and kept_idx).  tg_chain_create
- * validates them through the calls themselves (a failing call's status and
- * tg_last_error() come back unchanged and nothing is captured), captures the
- * chain on an internal stream and instantiates it.  The graph keeps the
- * pointers: the caller keeps every buffer alive and refills inputs in place.
- * tg_chain_launch enqueues one replay on `stream`; replays on one stream are
- * ordered and may not overlap a replay of the same chain on another stream
- * (they share the workspace and outputs).  tg_chain_destroy frees the graph
- * (NULL is a no-op).  Creating a chain allocates the runtime's graph objects
- * (host memory and whatever the runtime keeps per graph); replays allocate
- * nothing.
+ * NULL, selects tg_bias_attn_fwd_ws; the kv_ fields, if kv_L > 0, add
+ * tg_kv_gather with the desc's T, N, Hkv, D and kept_idx), with these
+ * differences that make one graph serve a bucket of prompts:
+ *   - N is a capacity.  The gather, the KV gather and the attention read the
+ *     kept count from n_kept (device memory the select writes) at every
+ *     replay: kept rows r >= n_kept are padding (zero residual and KV rows,
+ *     pos_kept -1, score_kept 0, attention output 0 and lse -inf), and keys
+ *     at or past n_kept are masked.  A kept count above N keeps its first N
+ *     rows (n_kept still holds the full count, so the caller can see it).
+ *   - prompt_len: NULL (T is the prompt's length), or a device int32 read at
+ *     every replay, 0 <= *prompt_len <= T: the gate and the select then take
+ *     only tokens [0, *prompt_len) of the T-token buffers (later tokens are
+ *     neither scored, kept nor counted).  T, and the buffers, are then the
+ *     bucket's capacity: a graph captured at (T, N) serves every prompt up
+ *     to T tokens whose kept count is at most N, with its inputs refilled in
+ *     place and *prompt_len set before the replay.
+ * tg_chain_create validates the arguments through the calls themselves (a
+ * failing call's status and tg_last_error() come back unchanged and nothing
+ * is captured), captures the chain on an internal stream and instantiates
+ * it.  The graph keeps the pointers: the caller keeps every buffer alive and
+ * refills inputs in place.  tg_chain_launch enqueues one replay on
+ * `stream`; replays on one stream are ordered and may not overlap a replay
+ * of the same chain on another stream (they share the workspace and
+ * outputs).  tg_chain_destroy frees the graph (NULL is a no-op).  Creating a
+ * chain allocates the runtime's graph objects (host memory and whatever the
+ * runtime keeps per graph); replays allocate nothing.
  * ------------------------------------------------------------------------ */
 typedef struct tg_chain tg_chain;
 
@@ -445,6 +459,8 @@ typedef struct tg_chain_desc {
   /* optional workspace of tg_bias_attn_fwd_ws (NULL: unsplit attention) */
   void* attn_workspace;
   size_t attn_workspace_bytes;
+  /* optional run-time prompt length: NULL, or a device int32 (see above) */
+  const int32_t* prompt_len;
 } tg_chain_desc;
 
 tg_status tg_chain_create(const tg_chain_desc* desc, tg_chain** chain);

@@ -84,6 +84,7 @@ class ChainDesc(ctypes.Structure):
         ("causal", _I), ("out", _P), ("lse", _P),
         ("kv_L", _I64), ("kv_k_cache", _P), ("kv_v_cache", _P), ("kv_k_kept", _P),
         ("kv_v_kept", _P), ("attn_workspace", _P), ("attn_workspace_bytes", ctypes.c_size_t),
+        ("prompt_len", _P),
     ]
 
 
@@ -334,11 +335,15 @@ def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, wor
                     out, w1_packed=False, b2=0.0, rms_weight=None, b1=None, eps=1e-6,
                     q_scale=None, softmax_scale=0.0, causal=True, lse=None,
                     kv_k_cache=None, kv_v_cache=None, kv_k_kept=None, kv_v_kept=None,
-                    attn_workspace=None):
+                    attn_workspace=None, prompt_len=None):
     """Capture gate -> top-K -> gather -> bias attention into one HIP graph.
     Every argument is the tensor the corresponding call would take; the graph
-    keeps their addresses, so refill inputs in place between launches."""
+    keeps their addresses, so refill inputs in place between launches.  N is
+    a capacity (rows past the device kept count are padding); ``prompt_len``
+    (a 1-element int32 device tensor, or None) makes T a capacity too: the
+    replay reads the prompt's length from it."""
     lib = load()
+    _dev(prompt_len, "prompt_len", torch.int32, allow_none=True)
     T, d = resid.shape
     h = w2.shape[0]
     Nq, Hq, D = q.shape
@@ -358,12 +363,14 @@ def tg_chain_create(*, resid, prunable, w1, w2, scores, K, kept_idx, n_kept, wor
         kv_k_cache=_addr(kv_k_cache), kv_v_cache=_addr(kv_v_cache),
         kv_k_kept=_addr(kv_k_kept), kv_v_kept=_addr(kv_v_kept),
         attn_workspace=_addr(attn_workspace),
-        attn_workspace_bytes=0 if attn_workspace is None else attn_workspace.numel())
+        attn_workspace_bytes=0 if attn_workspace is None else attn_workspace.numel(),
+        prompt_len=_addr(prompt_len))
     h_out = ctypes.c_void_p()
     _check(lib.tg_chain_create(ctypes.byref(desc), ctypes.byref(h_out)), "tg_chain_create")
     keep = [resid, prunable, w1, w2, scores, kept_idx, n_kept, workspace, resid_kept,
             pos_kept, score_kept, q, k, v, attn_key_score, gain, out, rms_weight, b1,
-            q_scale, lse, kv_k_cache, kv_v_cache, kv_k_kept, kv_v_kept, attn_workspace]
+            q_scale, lse, kv_k_cache, kv_v_cache, kv_k_kept, kv_v_kept, attn_workspace,
+            prompt_len]
     return TgChain(h_out, keep)
 
 

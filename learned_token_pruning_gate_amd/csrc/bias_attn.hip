@@ -156,7 +156,8 @@ attn_bf16_kernel(
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     uint16_t* __restrict__ out, float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
-    int32_t n_pblocks, int32_t n_hgroups, std::conditional_t<SPLIT, SplitLaunch, NoSplit> sp) {
+    int32_t n_pblocks, int32_t n_hgroups, const int32_t* __restrict__ n_dyn,
+    std::conditional_t<SPLIT, SplitLaunch, NoSplit> sp) {
   static_assert(!SPLIT || KS == 1, "a split chunk runs one key stream");
   static_assert(QW == 4 || (QW == 8 && KS == 1 && !SPLIT), "8 waves: one key stream, unsplit");
   constexpr int PB = 32 * (QW / HPW);       // query positions per workgroup
@@ -179,6 +180,12 @@ attn_bf16_kernel(
   const int hg = blockIdx.x % n_hgroups;
   const int G = Hq / Hkv;
   const int hw = wave % HPW;
+  // Ne: the kept count read at run time (N is then the capacity the launch
+  // and its buffers are sized for): keys at or past it are masked, and query
+  // rows at or past it are padding, written as O = 0, lse = -inf
+  const int Ne = n_dyn != nullptr ? min(N, max(*n_dyn, 0)) : N;
+  // key tiles with a visible key for query block p
+  auto live_tiles = [&](int p) { return p * PB >= Ne ? 0 : row_tiles(p, PB, Ne, CAUSAL); };
   const int head = hg * HPW + hw;
   const int kvh = (hg * HPW) / G;
 
@@ -264,7 +271,7 @@ attn_bf16_kernel(
   qf[DK] = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
                                               : u32x4{0, 0, 0, 0});
   float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
-  const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;   // last visible key
+  const int lim = CAUSAL ? min(my_q, Ne - 1) : Ne - 1;   // last visible key
 
   // ---- running state --------------------------------------------------------
   f32x16 o[DB];
@@ -324,7 +331,7 @@ attn_bf16_kernel(
     }
 
     // causal / tail mask (only tiles that reach past a query or past N)
-    const bool need_mask = (CAUSAL && k0 + kBK - 1 > pos0) || (k0 + kBK > N);
+    const bool need_mask = (CAUSAL && k0 + kBK - 1 > pos0) || (k0 + kBK > Ne);
     if (need_mask) {
       const int rel = lim - k0 - 4 * hh;   // key index k0 + 4hh + c is visible iff c <= rel
 #pragma unroll
@@ -486,7 +493,8 @@ attn_bf16_kernel(
       return;
     }
   }
-  const bool empty = !(l_tot > 0.0f) || m_run == -INFINITY;  // no visible key
+  // no visible key, or a padding row
+  const bool empty = !(l_tot > 0.0f) || m_run == -INFINITY || my_q >= Ne;
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (q_ok) {
     uint16_t* op = out + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D;
@@ -518,12 +526,12 @@ attn_bf16_kernel(
           nt > sp.a.ctiles
               ? (static_cast<size_t>(n_pblocks - 1 - p) * sp.a.nchunk + c) * n_hgroups + hg
               : kNoSlot;
-      run_item(p, t0, min(t0 + sp.a.ctiles, nt), nt, slot);
+      run_item(p, t0, min(t0 + sp.a.ctiles, live_tiles(p)), nt, slot);
     }
   } else {
     const int prank = blockIdx.x / n_hgroups;
     const int pblock = CAUSAL ? n_pblocks - 1 - prank : prank;
-    const int nt = row_tiles(pblock, PB, N, CAUSAL);
+    const int nt = live_tiles(pblock);
     run_item(pblock, 0, nt, nt, kNoSlot);
   }
 }
@@ -538,7 +546,8 @@ template <int D, int HPW, bool CAUSAL>
 __global__ __launch_bounds__(256) void attn_merge_kernel(SplitArgs sp, uint16_t* __restrict__ out,
                                                          float* __restrict__ lse, int32_t N,
                                                          int32_t Hq, int32_t n_pblocks,
-                                                         int32_t n_hgroups) {
+                                                         int32_t n_hgroups,
+                                                         const int32_t* __restrict__ n_dyn) {
   constexpr int PB = 32 * (4 / HPW);
   constexpr int DB = D / 32;
   const int lane = threadIdx.x & 63;
@@ -589,7 +598,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SplitArgs sp, uint16_t*
           acc[j][i] = fmaf(w, static_cast<float>(ov[c][j >> 1][4 * (j & 1) + i]), acc[j][i]);
     }
   }
-  const bool empty = !(l_tot > 0.0f) || m_max == -INFINITY;
+  // no visible key, or a padding row past a run-time kept count
+  const bool empty = !(l_tot > 0.0f) || m_max == -INFINITY ||
+                     (n_dyn != nullptr && my_q >= *n_dyn);
   const float inv = empty ? 0.0f : 1.0f / l_tot;
   if (my_q >= N) return;
   uint16_t* op = out + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D +
@@ -614,11 +625,20 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const float* __restrict__ key_score, const float* __restrict__ gain,
     const float* __restrict__ q_scale, float scale, int causal, float* __restrict__ out,
-    float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv) {
+    float* __restrict__ lse, int32_t N, int32_t Hq, int32_t Hkv,
+    const int32_t* __restrict__ n_dyn) {
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (idx >= static_cast<int64_t>(N) * Hq) return;
   const int r = static_cast<int>(idx / Hq);
   const int h = static_cast<int>(idx % Hq);
+  // run-time kept count (N: capacity): later rows are padding, keys masked
+  const int Ne = n_dyn != nullptr ? min(N, max(*n_dyn, 0)) : N;
+  if (r >= Ne) {
+    float* op = out + (static_cast<int64_t>(r) * Hq + h) * D;
+    for (int e = 0; e < D; ++e) op[e] = 0.0f;
+    if (lse) lse[static_cast<int64_t>(h) * N + r] = -INFINITY;
+    return;
+  }
   const int kvh = h / (Hq / Hkv);
   const float c = q_scale ? q_scale[r] : 1.0f;
   const float g = key_score ? gain[h] : 0.0f;
@@ -630,7 +650,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
     acc[e] = 0.0f;
   }
   float m = -INFINITY, l = 0.0f;
-  const int nk = causal ? r + 1 : N;
+  const int nk = causal ? r + 1 : Ne;
   for (int j = 0; j < nk; ++j) {
     const float* kp = k + (static_cast<int64_t>(j) * Hkv + kvh) * D;
     float dot = 0.0f;
@@ -690,6 +710,7 @@ struct AttnArgs {
   int32_t N, Hq, Hkv;
   bool causal, has_bias, has_qs;
   hipStream_t s;
+  const int32_t* n_dyn;   // run-time kept count, or NULL
 };
 
 // Key-chunk split of a bf16 launch (ctiles == 0: the launch runs unsplit).
@@ -840,7 +861,8 @@ template <int D, int HPW, bool CAUSAL, int KS, bool SPLIT, typename SP, int QW =
 void launch_bf16_attn_ks(const AttnArgs& a, dim3 grid, int32_t npb, int32_t nhg, const SP& sp) {
 #define TG_ATTN_LAUNCH(B, Q)                                                                 \
   attn_bf16_kernel<D, HPW, KS, QW, CAUSAL, B, Q, SPLIT><<<grid, dim3(64 * QW * KS), 0, a.s>>>( \
-      a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.out, a.lse, a.N, a.Hq, a.Hkv, npb, nhg, sp)
+      a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.out, a.lse, a.N, a.Hq, a.Hkv, npb, nhg,   \
+      a.n_dyn, sp)
   if (a.has_bias) {
     if (a.has_qs) TG_ATTN_LAUNCH(true, true); else TG_ATTN_LAUNCH(true, false);
   } else {
@@ -868,7 +890,7 @@ void launch_bf16_attn(const AttnArgs& a, const SplitPlan& pl, void* workspace) {
           a, dim3(static_cast<uint32_t>(pl.n_bins * nhg)), npb, nhg, sl);
       attn_merge_kernel<D, HPW, CAUSAL>
           <<<dim3(static_cast<uint32_t>(pl.n_split_rows * (D / 32) * nhg)), dim3(256), 0, a.s>>>(
-              sl.a, a.out, a.lse, a.N, a.Hq, npb, nhg);
+              sl.a, a.out, a.lse, a.N, a.Hq, npb, nhg, a.n_dyn);
       return;
     }
   }
@@ -901,7 +923,8 @@ void launch_bf16_attn_c(const AttnArgs& a, const SplitPlan& pl, void* workspace)
 tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, const void* q,
                    const void* k, const void* v, const float* key_score, const float* gain,
                    const float* q_scale, float softmax_scale, int causal, void* out,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream,
+                   const int32_t* n_dyn) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
     return fail(TG_ERR_INVALID_ARGUMENT, "tg_bias_attn_fwd: unknown dtype %d", (int)dt);
   if (N < 0 || N > kMaxTokens || Hq < 1 || Hkv < 1 || Hq > 65536 || Hkv > 65536)
@@ -952,17 +975,17 @@ tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, c
       attn_f32_kernel<64><<<grid, dim3(128), 0, s>>>(
           static_cast<const float*>(q), static_cast<const float*>(k),
           static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
-          static_cast<float*>(out), lse, n, hq, hkv);
+          static_cast<float*>(out), lse, n, hq, hkv, n_dyn);
     else if (D == 256)
       attn_f32_kernel<256><<<grid, dim3(128), 0, s>>>(
           static_cast<const float*>(q), static_cast<const float*>(k),
           static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
-          static_cast<float*>(out), lse, n, hq, hkv);
+          static_cast<float*>(out), lse, n, hq, hkv, n_dyn);
     else
       attn_f32_kernel<128><<<grid, dim3(128), 0, s>>>(
           static_cast<const float*>(q), static_cast<const float*>(k),
           static_cast<const float*>(v), key_score, gain, q_scale, scale, causal ? 1 : 0,
-          static_cast<float*>(out), lse, n, hq, hkv);
+          static_cast<float*>(out), lse, n, hq, hkv, n_dyn);
     return check_launch("tg_bias_attn_fwd");
   }
   const int64_t G = Hq / Hkv;
@@ -970,7 +993,7 @@ tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, c
   const AttnArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                    static_cast<const uint16_t*>(v), key_score, gain, q_scale, scale,
                    static_cast<uint16_t*>(out), lse, n, hq, hkv, causal != 0,
-                   key_score != nullptr, q_scale != nullptr, s};
+                   key_score != nullptr, q_scale != nullptr, s, n_dyn};
 #define TG_ATTN_DISPATCH(DD, HH) launch_bf16_attn_c<DD, HH>(a, pl, workspace)
   if (D == 256) {
     if (hpw == 4) TG_ATTN_DISPATCH(256, 4);
@@ -990,6 +1013,16 @@ tg_status attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D, c
 }
 
 }  // namespace
+
+tg_status bias_attn_call(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv, int64_t D,
+                         const void* q, const void* k, const void* v, const float* key_score,
+                         const float* gain, const float* q_scale, float softmax_scale,
+                         int causal, void* out, float* lse, void* workspace,
+                         size_t workspace_bytes, void* stream, const int32_t* n_dyn) {
+  return attn_fwd(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale, softmax_scale, causal,
+                  out, lse, workspace, workspace_bytes, stream, n_dyn);
+}
+
 }  // namespace tg
 
 extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
@@ -997,8 +1030,8 @@ extern "C" tg_status tg_bias_attn_fwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
                                       const float* key_score, const float* gain,
                                       const float* q_scale, float softmax_scale, int causal,
                                       void* out, float* lse, void* stream) {
-  return tg::attn_fwd(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale, softmax_scale,
-                      causal, out, lse, nullptr, 0, stream);
+  return tg::bias_attn_call(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale,
+                            softmax_scale, causal, out, lse, nullptr, 0, stream, nullptr);
 }
 
 extern "C" size_t tg_bias_attn_workspace_size(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
@@ -1015,6 +1048,7 @@ extern "C" tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int
                                          const float* q_scale, float softmax_scale, int causal,
                                          void* out, float* lse, void* workspace,
                                          size_t workspace_bytes, void* stream) {
-  return tg::attn_fwd(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale, softmax_scale,
-                      causal, out, lse, workspace, workspace_bytes, stream);
+  return tg::bias_attn_call(dt, N, Hq, Hkv, D, q, k, v, key_score, gain, q_scale,
+                            softmax_scale, causal, out, lse, workspace, workspace_bytes, stream,
+                            nullptr);
 }

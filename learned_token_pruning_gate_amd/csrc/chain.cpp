@@ -1,8 +1,14 @@
 // chain.cpp -- the four calls of the path captured once as a HIP graph and
 // replayed (TokenGate pages: ai.info summary "Key Contributions" item 4, the
-// graph-captured serving recipe).  Host code only: the capture records the
-// kernels that the four entry points enqueue; nothing here runs on the GPU
-// by itself.
+// serving recipe captures the pruned forward pass as a graph per padded
+// length).  Host code only: the capture records the kernels that the four
+// calls enqueue; nothing here runs on the GPU by itself.
+//
+// Sizes in the graph are capacities.  The gather, the KV gather and the
+// attention read the kept count from the select's n_kept at every replay
+// (rows past it are padding), and with a prompt-length pointer the gate and
+// the select read the prompt's length too, so one graph serves every prompt
+// of its bucket.
 #include <new>
 
 #include "tg_common.hpp"
@@ -18,34 +24,33 @@ namespace {
 // joins `s` after the attention; fork/join are event edges of the capture.
 tg_status run_chain(const tg_chain_desc& d, hipStream_t s, hipStream_t side, hipEvent_t fork,
                     hipEvent_t join) {
-  tg_status st =
-      d.w1_packed
-          ? tg_gate_score_packed(d.dt, d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
-                                 d.rms_weight, d.eps, d.w1, d.b1, d.w2, d.b2, d.scores, s)
-          : tg_gate_score(d.dt, d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
-                          d.rms_weight, d.eps, d.w1, d.b1, d.w2, d.b2, d.scores, s);
+  using namespace tg;
+  tg_status st = gate_score_call(d.w1_packed ? "tg_gate_score_packed" : "tg_gate_score", d.dt,
+                                 d.T, d.d, d.h, d.resid, d.resid_row_stride, d.prunable,
+                                 d.rms_weight, d.eps, d.w1, d.w1_packed != 0, d.b1, d.w2, d.b2,
+                                 d.scores, s, d.prompt_len);
   if (st != TG_OK) return st;
-  st = tg_topk_select(d.T, d.scores, d.prunable, d.K, d.kept_idx, d.kept_capacity, d.n_kept,
-                      d.workspace, d.workspace_bytes, s);
+  st = topk_select_call(d.T, d.scores, d.prunable, d.K, d.kept_idx, d.kept_capacity, d.n_kept,
+                        d.workspace, d.workspace_bytes, s, d.prompt_len);
   if (st != TG_OK) return st;
-  st = tg_compact_gather(d.dt, d.T, d.N, d.d, d.resid, d.resid_row_stride, d.scores,
-                         d.kept_idx, d.resid_kept, d.kept_row_stride, d.pos_kept, d.score_kept,
-                         s);
+  st = compact_gather_call(d.dt, d.T, d.N, d.d, d.resid, d.resid_row_stride, d.scores,
+                           d.kept_idx, d.resid_kept, d.kept_row_stride, d.pos_kept,
+                           d.score_kept, s, d.n_kept);
   if (st != TG_OK) return st;
   const bool kv = d.kv_L > 0;
   if (kv) {
     if (hipEventRecord(fork, s) != hipSuccess || hipStreamWaitEvent(side, fork, 0) != hipSuccess)
-      return tg::fail(TG_ERR_LAUNCH, "tg_chain_create: could not fork the KV gather");
-    st = tg_kv_gather(d.dt, d.kv_L, d.T, d.N, d.Hkv, d.D, d.kv_k_cache, d.kv_v_cache, d.kept_idx,
-                      d.kv_k_kept, d.kv_v_kept, side);
+      return fail(TG_ERR_LAUNCH, "tg_chain_create: could not fork the KV gather");
+    st = kv_gather_call(d.dt, d.kv_L, d.T, d.N, d.Hkv, d.D, d.kv_k_cache, d.kv_v_cache,
+                        d.kept_idx, d.kv_k_kept, d.kv_v_kept, side, d.n_kept);
     if (st != TG_OK) return st;
   }
-  st = tg_bias_attn_fwd_ws(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score,
-                           d.gain, d.q_scale, d.softmax_scale, d.causal, d.out, d.lse,
-                           d.attn_workspace, d.attn_workspace_bytes, s);
+  st = bias_attn_call(d.dt, d.N, d.Hq, d.Hkv, d.D, d.q, d.k, d.v, d.attn_key_score, d.gain,
+                      d.q_scale, d.softmax_scale, d.causal, d.out, d.lse, d.attn_workspace,
+                      d.attn_workspace_bytes, s, d.n_kept);
   if (st != TG_OK) return st;
   if (kv && (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(s, join, 0) != hipSuccess))
-    return tg::fail(TG_ERR_LAUNCH, "tg_chain_create: could not join the KV gather");
+    return fail(TG_ERR_LAUNCH, "tg_chain_create: could not join the KV gather");
   return TG_OK;
 }
 

@@ -22,12 +22,15 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(
     const float* __restrict__ scores, const int32_t* __restrict__ kept_idx,
     uint8_t* __restrict__ dst, int64_t dst_stride_bytes, int64_t row_vecs,
     int32_t T, int32_t N, int32_t* __restrict__ pos_kept,
-    float* __restrict__ score_kept) {
+    float* __restrict__ score_kept, const int32_t* __restrict__ n_dyn) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * kRowsPerBlock + wave;
   if (r >= N) return;
-  const int32_t t = kept_idx[r];
+  // with a run-time kept count (N is then the capacity), rows at or past it
+  // are written as padding: zero row, position -1, score 0
+  const bool live = n_dyn == nullptr || r < *n_dyn;
+  const int32_t t = live ? kept_idx[r] : -1;
   const bool valid = (t >= 0) && (t < T);
   if (lane == 0) {
     if (pos_kept) pos_kept[r] = valid ? t : -1;
@@ -66,26 +69,23 @@ template <typename V>
 tg_status launch(const void* resid, int64_t src_stride_bytes, const float* scores,
                  const int32_t* kept_idx, void* resid_kept, int64_t dst_stride_bytes,
                  int64_t row_bytes, int64_t T, int64_t N, int32_t* pos_kept,
-                 float* score_kept, hipStream_t stream) {
+                 float* score_kept, hipStream_t stream, const int32_t* n_dyn) {
   const int64_t blocks = (N + kRowsPerBlock - 1) / kRowsPerBlock;
   gather_rows_kernel<V><<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream>>>(
       static_cast<const uint8_t*>(resid), src_stride_bytes, scores, kept_idx,
       static_cast<uint8_t*>(resid_kept), dst_stride_bytes,
       row_bytes / static_cast<int64_t>(sizeof(V)), static_cast<int32_t>(T),
-      static_cast<int32_t>(N), pos_kept, score_kept);
+      static_cast<int32_t>(N), pos_kept, score_kept, n_dyn);
   return check_launch("tg_compact_gather");
 }
 
 }  // namespace
-}  // namespace tg
 
-extern "C" tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
-                                       const void* resid, int64_t resid_row_stride,
-                                       const float* scores, const int32_t* kept_idx,
-                                       void* resid_kept, int64_t kept_row_stride,
-                                       int32_t* pos_kept, float* score_kept,
-                                       void* stream) {
-  using namespace tg;
+tg_status compact_gather_call(tg_dtype dt, int64_t T, int64_t N, int64_t d, const void* resid,
+                              int64_t resid_row_stride, const float* scores,
+                              const int32_t* kept_idx, void* resid_kept,
+                              int64_t kept_row_stride, int32_t* pos_kept, float* score_kept,
+                              void* stream, const int32_t* n_dyn) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
     return fail(TG_ERR_INVALID_ARGUMENT, "tg_compact_gather: unknown dtype %d", (int)dt);
   if (T < 0 || T > kMaxTokens || N < 0 || N > kMaxTokens || d < 1)
@@ -121,12 +121,25 @@ extern "C" tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_
                     aligned(resid, 16) && aligned(resid_kept, 16));
   if (v16)
     return launch<Vec16>(resid, sstride, scores, kept_idx, resid_kept, dstride, row_bytes,
-                         T, N, pos_kept, score_kept, s);
+                         T, N, pos_kept, score_kept, s, n_dyn);
   const bool v4 = row_bytes % 4 == 0 && sstride % 4 == 0 && dstride % 4 == 0 &&
                   aligned(resid, 4) && aligned(resid_kept, 4);
   if (v4)
     return launch<Vec4>(resid, sstride, scores, kept_idx, resid_kept, dstride, row_bytes,
-                        T, N, pos_kept, score_kept, s);
+                        T, N, pos_kept, score_kept, s, n_dyn);
   return launch<Vec2>(resid, sstride, scores, kept_idx, resid_kept, dstride, row_bytes, T,
-                      N, pos_kept, score_kept, s);
+                      N, pos_kept, score_kept, s, n_dyn);
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
+                                       const void* resid, int64_t resid_row_stride,
+                                       const float* scores, const int32_t* kept_idx,
+                                       void* resid_kept, int64_t kept_row_stride,
+                                       int32_t* pos_kept, float* score_kept,
+                                       void* stream) {
+  return tg::compact_gather_call(dt, T, N, d, resid, resid_row_stride, scores, kept_idx,
+                                 resid_kept, kept_row_stride, pos_kept, score_kept, stream,
+                                 nullptr);
 }

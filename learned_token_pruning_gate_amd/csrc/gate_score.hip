@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256, kMinWG) void gate_bf16_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     const float* __restrict__ gamma, float eps, const uint16_t* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2,
-    float* __restrict__ scores, int32_t T, int32_t d) {
+    float* __restrict__ scores, int32_t T, int32_t d, const int32_t* __restrict__ t_dyn) {
   constexpr int RPT = TM / 32;          // staged rows per thread
   constexpr int MT = TM / 16;           // 16-row MFMA tiles per wave
   __shared__ __attribute__((aligned(16))) uint16_t xs[2][TM * kPitch];
@@ -57,6 +57,10 @@ __global__ __launch_bounds__(256, kMinWG) void gate_bf16_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * TM;
+  if (t_dyn != nullptr) {   // the prompt's length, read at run time (T is the capacity)
+    T = min(T, max(*t_dyn, 0));
+    if (row0 >= T) return;
+  }
 
   // staging role: row (tid/8) + 32 i, 16-byte chunk tid % 8 of the stage.
   // Loads go through buffer resources: an offset past the end reads zeros,
@@ -354,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     float eps, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
     const float* __restrict__ w2, float b2, float* __restrict__ scores, int32_t T, int32_t d,
-    int32_t h) {
+    int32_t h, const int32_t* __restrict__ t_dyn) {
   constexpr int TM = 64;
   constexpr int DEPTH = kDepth;
   constexpr int R = DEPTH + 1;                 // ring length
@@ -374,6 +378,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   const int lrow = lane & 15;
   const int lgrp = lane >> 4;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * TM;
+  if (t_dyn != nullptr) {   // the prompt's length, read at run time (T is the capacity)
+    T = min(T, max(*t_dyn, 0));
+    if (row0 >= T) return;
+  }
 
   if (tid == 0) s_any = 0;
   __syncthreads();
@@ -635,9 +643,11 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(
     const float* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     const float* __restrict__ gamma, float eps, const float* __restrict__ w1,
     const float* __restrict__ b1, const float* __restrict__ w2, float b2,
-    float* __restrict__ scores, int32_t T, int32_t d, int32_t h) {
+    float* __restrict__ scores, int32_t T, int32_t d, int32_t h,
+    const int32_t* __restrict__ t_dyn) {
   const int lane = threadIdx.x & 63;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
   if (t >= T) return;
   if (!prunable[t]) {
     if (lane == 0) scores[t] = 0.0f;
@@ -668,39 +678,44 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(
 template <int TM, int NT, bool FAST>
 void launch_bf16_f(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint16_t* x,
                    int64_t ld, const uint8_t* p, const float* g, float eps, const uint16_t* w1,
-                   const float* b1, const float* w2, float b2, float* out, int32_t d) {
+                   const float* b1, const float* w2, float b2, float* out, int32_t d,
+                   const int32_t* t_dyn) {
   if (has_gamma)
     gate_bf16_kernel<TM, NT, true, FAST><<<grid, dim3(256), static_cast<size_t>(d) * 4, s>>>(
-        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d, t_dyn);
   else
     gate_bf16_kernel<TM, NT, false, FAST><<<grid, dim3(256), 0, s>>>(
-        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d);
+        x, ld, p, g, eps, w1, b1, w2, b2, out, static_cast<int32_t>(T), d, t_dyn);
 }
 
 template <int TM, int NT>
 void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint16_t* x,
                  int64_t ld, const uint8_t* p, const float* g, float eps, const uint16_t* w1,
-                 const float* b1, const float* w2, float b2, float* out, int32_t d) {
+                 const float* b1, const float* w2, float b2, float* out, int32_t d,
+                 const int32_t* t_dyn) {
   if (d % (2 * kKS) == 0)
-    launch_bf16_f<TM, NT, true>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d);
+    launch_bf16_f<TM, NT, true>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d,
+                                t_dyn);
   else
-    launch_bf16_f<TM, NT, false>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out, d);
+    launch_bf16_f<TM, NT, false>(has_gamma, T, grid, s, x, ld, p, g, eps, w1, b1, w2, b2, out,
+                                 d, t_dyn);
 }
 
 // Streaming kernel dispatch: h = 16 * NTW * NW.
 void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
                    const uint16_t* x, int64_t ld, const uint8_t* p, float eps,
-                   const uint16_t* w, const float* b1, const float* w2, float b2, float* out) {
+                   const uint16_t* w, const float* b1, const float* w2, float b2, float* out,
+                   const int32_t* t_dyn) {
   const dim3 grid(static_cast<uint32_t>((T + 63) / 64));
   const int32_t T32 = static_cast<int32_t>(T), h32 = static_cast<int32_t>(h);
 #define TG_GATE_STREAM(NTW, NW, NST)                                                         \
   do {                                                                                      \
     if (packed)                                                                             \
       gate_bf16_stream_kernel<NTW, NW, NST, true><<<grid, dim3(NW * 64), 0, s>>>(           \
-          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32);                                  \
+          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
     else                                                                                    \
       gate_bf16_stream_kernel<NTW, NW, NST, false><<<grid, dim3(NW * 64), 0, s>>>(          \
-          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32);                                  \
+          x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
   } while (0)
   if (h == 256 && d == 2048) TG_GATE_STREAM(2, 8, 32);   // Qwen3-1.7B hidden size, h = 256
   else if (h == 256) TG_GATE_STREAM(2, 8, 0);
@@ -710,11 +725,13 @@ void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
 #undef TG_GATE_STREAM
 }
 
-tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int64_t h,
+}  // namespace
+
+tg_status gate_score_call(const char* fn, tg_dtype dt, int64_t T, int64_t d, int64_t h,
                           const void* resid, int64_t resid_row_stride, const uint8_t* prunable,
                           const float* rms_weight, float eps, const void* w1, bool packed,
                           const float* b1, const float* w2, float b2, float* scores,
-                          void* stream) {
+                          void* stream, const int32_t* t_dyn) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
     return fail(TG_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", fn, (int)dt);
   if (T < 0 || T > kMaxTokens || d < 1 || h < 1 || d > kMaxTokens || h > kMaxTokens)
@@ -750,7 +767,7 @@ tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int
     gate_f32_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, s>>>(
         static_cast<const float*>(resid), resid_row_stride, prunable, rms_weight, eps,
         static_cast<const float*>(w1), b1, w2, b2, scores, static_cast<int32_t>(T),
-        static_cast<int32_t>(d), static_cast<int32_t>(h));
+        static_cast<int32_t>(d), static_cast<int32_t>(h), t_dyn);
     return check_launch(fn);
   }
   if (d % 8 != 0)
@@ -771,26 +788,27 @@ tg_status gate_score_impl(const char* fn, tg_dtype dt, int64_t T, int64_t d, int
   const auto* w = static_cast<const uint16_t*>(w1);
   const int32_t d32 = static_cast<int32_t>(d);
   if (packed) {
-    launch_stream(true, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores);
+    launch_stream(true, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores,
+                  t_dyn);
     return check_launch(fn);
   }
   if (rms_weight == nullptr && d % kKS == 0 && d >= 2 * kKS) {
-    launch_stream(false, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores);
+    launch_stream(false, T, h, d32, s, x, resid_row_stride, prunable, eps, w, b1, w2, b2, scores,
+                  t_dyn);
     return check_launch(fn);
   }
   const bool g = rms_weight != nullptr;
   constexpr int TM = kTM;
   const dim3 grid(static_cast<uint32_t>((T + TM - 1) / TM));
   switch (h / 64) {
-    case 1: launch_bf16<TM, 1>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
-    case 2: launch_bf16<TM, 2>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
-    case 3: launch_bf16<TM, 3>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
-    default: launch_bf16<TM, 4>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32); break;
+    case 1: launch_bf16<TM, 1>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32, t_dyn); break;
+    case 2: launch_bf16<TM, 2>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32, t_dyn); break;
+    case 3: launch_bf16<TM, 3>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32, t_dyn); break;
+    default: launch_bf16<TM, 4>(g, T, grid, s, x, resid_row_stride, prunable, rms_weight, eps, w, b1, w2, b2, scores, d32, t_dyn); break;
   }
   return check_launch(fn);
 }
 
-}  // namespace
 }  // namespace tg
 
 extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
@@ -798,8 +816,8 @@ extern "C" tg_status tg_gate_score(tg_dtype dt, int64_t T, int64_t d, int64_t h,
                                    const uint8_t* prunable, const float* rms_weight, float eps,
                                    const void* w1, const float* b1, const float* w2, float b2,
                                    float* scores, void* stream) {
-  return tg::gate_score_impl("tg_gate_score", dt, T, d, h, resid, resid_row_stride, prunable,
-                             rms_weight, eps, w1, false, b1, w2, b2, scores, stream);
+  return tg::gate_score_call("tg_gate_score", dt, T, d, h, resid, resid_row_stride, prunable,
+                             rms_weight, eps, w1, false, b1, w2, b2, scores, stream, nullptr);
 }
 
 extern "C" tg_status tg_gate_score_packed(tg_dtype dt, int64_t T, int64_t d, int64_t h,
@@ -808,9 +826,9 @@ extern "C" tg_status tg_gate_score_packed(tg_dtype dt, int64_t T, int64_t d, int
                                           float eps, const void* w1_packed, const float* b1,
                                           const float* w2, float b2, float* scores,
                                           void* stream) {
-  return tg::gate_score_impl("tg_gate_score_packed", dt, T, d, h, resid, resid_row_stride,
+  return tg::gate_score_call("tg_gate_score_packed", dt, T, d, h, resid, resid_row_stride,
                              prunable, rms_weight, eps, w1_packed, true, b1, w2, b2, scores,
-                             stream);
+                             stream, nullptr);
 }
 
 extern "C" size_t tg_gate_w1_packed_bytes(tg_dtype dt, int64_t h, int64_t d) {

@@ -22,12 +22,13 @@ constexpr int kPairsPerBlock = 4;   // one wave per (layer, kept token)
 __global__ __launch_bounds__(256) void kv_gather_kernel(
     const uint8_t* __restrict__ kc, const uint8_t* __restrict__ vc,
     const int32_t* __restrict__ kept_idx, uint8_t* __restrict__ ko, uint8_t* __restrict__ vo,
-    int64_t nvec, int32_t L, int32_t T, int32_t N) {
+    int64_t nvec, int32_t L, int32_t T, int32_t N, const int32_t* __restrict__ n_dyn) {
   const int lane = threadIdx.x & 63;
   const int64_t pair = static_cast<int64_t>(blockIdx.x) * kPairsPerBlock + (threadIdx.x >> 6);
   if (pair >= static_cast<int64_t>(L) * N) return;
   const int64_t l = pair / N, r = pair - l * N;
-  const int32_t t = kept_idx[r];
+  // with a run-time kept count (N: capacity), rows at or past it are zero
+  const int32_t t = (n_dyn == nullptr || r < *n_dyn) ? kept_idx[r] : -1;
   const bool valid = t >= 0 && t < T;   // an out-of-range index yields zero rows
   const int64_t row_bytes = nvec * 16;
   const int64_t so = (l * T + (valid ? t : 0)) * row_bytes, dof = pair * row_bytes;
@@ -52,13 +53,10 @@ __global__ __launch_bounds__(256) void kv_gather_kernel(
 }
 
 }  // namespace
-}  // namespace tg
 
-extern "C" tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv,
-                                  int64_t D, const void* k_cache, const void* v_cache,
-                                  const int32_t* kept_idx, void* k_kept, void* v_kept,
-                                  void* stream) {
-  using namespace tg;
+tg_status kv_gather_call(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv, int64_t D,
+                         const void* k_cache, const void* v_cache, const int32_t* kept_idx,
+                         void* k_kept, void* v_kept, void* stream, const int32_t* n_dyn) {
   if (dt != TG_DTYPE_F32 && dt != TG_DTYPE_BF16)
     return fail(TG_ERR_INVALID_ARGUMENT, "tg_kv_gather: unknown dtype %d", (int)dt);
   if (L < 0 || T < 0 || N < 0 || Hkv < 1 || D < 1 || T > kMaxTokens || N > kMaxTokens ||
@@ -89,6 +87,16 @@ extern "C" tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, 
   kv_gather_kernel<<<dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, as_stream(stream)>>>(
       static_cast<const uint8_t*>(k_cache), static_cast<const uint8_t*>(v_cache), kept_idx,
       static_cast<uint8_t*>(k_kept), static_cast<uint8_t*>(v_kept), row_bytes / 16,
-      static_cast<int32_t>(L), static_cast<int32_t>(T), static_cast<int32_t>(N));
+      static_cast<int32_t>(L), static_cast<int32_t>(T), static_cast<int32_t>(N), n_dyn);
   return check_launch("tg_kv_gather");
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_kv_gather(tg_dtype dt, int64_t L, int64_t T, int64_t N, int64_t Hkv,
+                                  int64_t D, const void* k_cache, const void* v_cache,
+                                  const int32_t* kept_idx, void* k_kept, void* v_kept,
+                                  void* stream) {
+  return tg::kv_gather_call(dt, L, T, N, Hkv, D, k_cache, v_cache, kept_idx, k_kept, v_kept,
+                            stream, nullptr);
 }

@@ -106,8 +106,10 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* s
 template <int PASS>
 __global__ __launch_bounds__(kThreads) void radix_hist_kernel(
     const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
-    int64_t per_block, uint32_t K, uint32_t n_compact_blocks, uint8_t* __restrict__ ws) {
+    int64_t per_block, uint32_t K, uint32_t n_compact_blocks, uint8_t* __restrict__ ws,
+    const int32_t* __restrict__ t_dyn) {
   constexpr int BITS = PASS == 2 ? 10 : 11;
+  if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
   constexpr int NB = 1 << BITS;
   constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
   constexpr int BPT = NB / kThreads;  // bins per thread in the resolve step
@@ -230,7 +232,8 @@ __device__ __forceinline__ uint64_t pack_desc(uint64_t flag, uint32_t a, uint32_
 __global__ __launch_bounds__(kThreads) void compact_kernel(
     const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
     int64_t per_block, uint8_t* __restrict__ ws, int32_t* __restrict__ kept_idx,
-    int64_t capacity, int32_t* __restrict__ n_kept) {
+    int64_t capacity, int32_t* __restrict__ n_kept, const int32_t* __restrict__ t_dyn) {
+  if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
   __shared__ uint32_t s_wave[kThreads / 64];
   __shared__ uint32_t s_ticket;
   __shared__ uint32_t s_pre_a, s_pre_b;
@@ -419,8 +422,9 @@ template <int MAXT>
 __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
     uint32_t K, int32_t* __restrict__ kept_idx, int64_t capacity,
-    int32_t* __restrict__ n_kept) {
+    int32_t* __restrict__ n_kept, const int32_t* __restrict__ t_dyn) {
   constexpr int NCOPY = MAXT <= 16384 ? 8 : 1;
+  if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
   __shared__ __attribute__((aligned(16))) uint32_t keys[MAXT];
   // the digit histograms and the resolved state, double-buffered by pass:
   // the next pass's histogram is cleared while wave 0 scans this one's
@@ -687,7 +691,8 @@ tg_status select_check(const char* fn, int64_t T, const float* scores, const uin
 // bytes, 256-byte aligned, all zero.
 tg_status select_launch(const char* fn, int64_t T, const float* scores,
                         const uint8_t* prunable, int64_t K, int32_t* kept_idx,
-                        int64_t kept_capacity, int32_t* n_kept, uint8_t* ws, hipStream_t s) {
+                        int64_t kept_capacity, int32_t* n_kept, uint8_t* ws, hipStream_t s,
+                        const int32_t* t_dyn) {
   if (T == 0) {
     write_zero_kernel<<<1, 1, 0, s>>>(n_kept);
     return check_launch(fn);
@@ -696,34 +701,35 @@ tg_status select_launch(const char* fn, int64_t T, const float* scores,
   if (T <= kLdsTokens && aligned(prunable, 16)) {
     if (T <= kLdsTokens / 2)
       select_one_wg_kernel<kLdsTokens / 2><<<dim3(1), dim3(kOneThreads), 0, s>>>(
-          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept);
+          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept, t_dyn);
     else
       select_one_wg_kernel<kLdsTokens><<<dim3(1), dim3(kOneThreads), 0, s>>>(
-          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept);
+          scores, prunable, static_cast<int32_t>(T), Kc, kept_idx, kept_capacity, n_kept, t_dyn);
     return check_launch(fn);
   }
   int64_t per_block = 0;
   const int64_t G = blocks_for(T, &per_block);
   const int32_t T32 = static_cast<int32_t>(T);
   radix_hist_kernel<0><<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block,
-                                                           Kc, static_cast<uint32_t>(G), ws);
+                                                           Kc, static_cast<uint32_t>(G), ws, t_dyn);
   radix_hist_kernel<1><<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block,
-                                                           Kc, static_cast<uint32_t>(G), ws);
+                                                           Kc, static_cast<uint32_t>(G), ws, t_dyn);
   radix_hist_kernel<2><<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block,
-                                                           Kc, static_cast<uint32_t>(G), ws);
+                                                           Kc, static_cast<uint32_t>(G), ws, t_dyn);
   compact_kernel<<<dim3(G), dim3(kThreads), 0, s>>>(scores, prunable, T32, per_block, ws,
-                                                     kept_idx, kept_capacity, n_kept);
+                                                     kept_idx, kept_capacity, n_kept, t_dyn);
   return check_launch(fn);
 }
 
 }  // namespace
 }  // namespace tg
 
-extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_t* prunable,
-                                    int64_t K, int32_t* kept_idx, int64_t kept_capacity,
-                                    int32_t* n_kept, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
-  using namespace tg;
+namespace tg {
+
+tg_status topk_select_call(int64_t T, const float* scores, const uint8_t* prunable, int64_t K,
+                           int32_t* kept_idx, int64_t kept_capacity, int32_t* n_kept,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           const int32_t* t_dyn) {
   tg_status st = select_check("tg_topk_select", T, scores, prunable, K, kept_idx,
                               kept_capacity, n_kept);
   if (st != TG_OK) return st;
@@ -736,7 +742,17 @@ extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_
       return fail(TG_ERR_WORKSPACE, "tg_topk_select: workspace must be 256-byte aligned");
   }
   return select_launch("tg_topk_select", T, scores, prunable, K, kept_idx, kept_capacity,
-                       n_kept, static_cast<uint8_t*>(workspace), as_stream(stream));
+                       n_kept, static_cast<uint8_t*>(workspace), as_stream(stream), t_dyn);
+}
+
+}  // namespace tg
+
+extern "C" tg_status tg_topk_select(int64_t T, const float* scores, const uint8_t* prunable,
+                                    int64_t K, int32_t* kept_idx, int64_t kept_capacity,
+                                    int32_t* n_kept, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  return tg::topk_select_call(T, scores, prunable, K, kept_idx, kept_capacity, n_kept,
+                              workspace, workspace_bytes, stream, nullptr);
 }
 
 extern "C" tg_status tg_topk_select_noalloc(int64_t T, const float* scores,
@@ -756,5 +772,6 @@ extern "C" tg_status tg_topk_select_noalloc(int64_t T, const float* scores,
   uint8_t* ws = nullptr;
   st = static_scratch(s, &ws);
   if (st != TG_OK) return st;
-  return select_launch(fn, T, scores, prunable, K, kept_idx, kept_capacity, n_kept, ws, s);
+  return select_launch(fn, T, scores, prunable, K, kept_idx, kept_capacity, n_kept, ws, s,
+                       nullptr);
 }
