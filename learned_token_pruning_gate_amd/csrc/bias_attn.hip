@@ -45,9 +45,11 @@
 //     the even and odd key tiles, each with its own LDS buffers, and merges
 //     their softmax states at the end; each wave's serial loop halves and
 //     two waves share every SIMD.
-//   * The bias gain_h*log2(e)*score_c is formed once per key tile and head
-//     in LDS; logits use exp2 with log2(e) folded into the scale; the output
-//     is rescaled only when some query's running max grows.
+//   * The bias gain_h*score_c (in dot-product units) is formed once per key
+//     tile and head in LDS, in the accumulator layout's key order, and is the
+//     initial value of the logit accumulators, so the MFMAs add the dot
+//     products to it; logits use exp2 with log2(e) folded into the scale;
+//     the output is rescaled only when some query's running max grows.
 //   * Workgroups are ordered longest-first (causal) and the KV head is the
 //     fastest-varying index, so consecutive workgroups -- which the
 //     dispatcher spreads over the 8 XCDs -- keep one KV head per XCD L2.
@@ -86,7 +88,7 @@ struct AttnSmem {
   static constexpr int SW = (D / 8 < 16 ? D / 8 : 16) - 1;
   uint16_t ks[kBK * D];
   uint16_t vs[kBK * D];
-  u32x2 bias[4][kBK];                       // per head: bf16 (hi | mid << 16, lo)
+  float bias[4][kBK];                       // per head, in accumulator order (bias_slot)
 };
 __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
@@ -100,14 +102,14 @@ __device__ __forceinline__ float bf16_val(uint32_t bits) {
 // far below it).
 constexpr float kMaskedLog2 = -524288.0f;
 
-// The bias enters the MFMA as three bf16 terms hi + mid + lo, which carry a
-// fp32 value to within 2^-25 of itself: (hi | mid << 16, lo).
-__device__ __forceinline__ u32x2 split_bf16_triple(float v) {
-  const uint32_t hi = bf16_bits(v);
-  const float r1 = v - bf16_val(hi);
-  const uint32_t mid = bf16_bits(r1);
-  const uint32_t lo = bf16_bits(r1 - bf16_val(mid));
-  return u32x2{hi | (mid << 16), lo};
+// The bias of a key tile is the initial value of the logit accumulators: in
+// the 32x32 accumulator layout, lane (query, half hh) holds in register r of
+// key block kb the logit of key 32 kb + 8 (r / 4) + r % 4 + 4 hh, so the 64
+// biases are stored in that order, and each lane reads its 16 with four
+// 16-byte reads that every lane of its half shares (LDS broadcasts).
+__device__ __forceinline__ int bias_slot(int key) {
+  const int rem = key & 31;
+  return (key & 32) + ((rem >> 2) & 1) * 16 + (rem >> 3) * 4 + (rem & 3);
 }
 
 // ---- key-chunk split ---------------------------------------------------------
@@ -195,9 +197,8 @@ attn_bf16_kernel(
 
   // ---- staging -------------------------------------------------------------
   const float inv_scale = 1.0f / scale;
-  // A -inf score becomes the bias -2^100 in dot-product units (exact in
-  // bf16, so the bias k-step adds it exactly and it absorbs any finite dot
-  // product).  Its logit, -2^100 scale log2(e) c_r log2 units, falls below
+  // A -inf score becomes the bias -2^100 in dot-product units (exact, and it
+  // absorbs any finite dot product).  Its logit, -2^100 scale log2(e) c_r log2 units, falls below
   // kMaskedLog2 whenever scale * c_r > 2^-80, and its weight underflows to
   // exactly 0, as deleting the key would give.
   const float masked_bias = -0x1p100f;
@@ -235,8 +236,8 @@ attn_bf16_kernel(
   };
   auto store_bias = [&](Smem& b) {
     if (HAS_BIAS && tid < HPW * kBK)
-      b.bias[tid / kBK][bias_key] = split_bf16_triple(
-          sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale);
+      b.bias[tid / kBK][bias_slot(bias_key)] =
+          sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale;
   };
   // vmcnt(0), other counters untouched: every direct-to-LDS load of this
   // wave has landed (each wave then passes the barrier)
@@ -256,10 +257,8 @@ attn_bf16_kernel(
   const float ac = scale * kLog2e * cr;
 
   // Q^T as MFMA B operand (exact bf16): lane (query l32, half hh) holds dims
-  // 16 ks + 8 hh .. +7.  k-step DK is the extra one: [1, 1, 1, 0...] in the
-  // hh = 0 half, matched on the key side by [bias'_hi, bias'_mid, bias'_lo,
-  // 0...], so the MFMA adds the gate bias to every logit.
-  bf16x8 qf[DK + 1];
+  // 16 ks + 8 hh .. +7.
+  bf16x8 qf[DK];
   {
     const uint32_t base = static_cast<uint32_t>(my_q) * q_row +
                           static_cast<uint32_t>(head) * D * 2 + 16u * hh;
@@ -268,8 +267,6 @@ attn_bf16_kernel(
       qf[ks] = __builtin_bit_cast(bf16x8,
                                   __builtin_amdgcn_raw_buffer_load_b128(q_rs, base + 32u * ks, 0, 0));
   }
-  qf[DK] = __builtin_bit_cast(bf16x8, hh == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0, 0}
-                                              : u32x4{0, 0, 0, 0});
   float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
   const int lim = CAUSAL ? min(my_q, Ne - 1) : Ne - 1;   // last visible key
 
@@ -302,13 +299,26 @@ attn_bf16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     if (KS == 1 || t < t_end) {   // uniform per wave: a stream may idle in the last round
 
-    // S'^T = K' Q'^T = <q, k> + bias'; the two 32-key halves are independent
-    // accumulation chains, interleaved so neither waits on its own last MFMA
+    // S^T = bias' + K Q^T: the accumulators start from the tile's bias (in
+    // dot-product units, zero without one); the two 32-key halves are
+    // independent accumulation chains, interleaved so neither waits on its
+    // own last MFMA
     f32x16 s[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      if (HAS_BIAS) {
+        const f32x4* bp = reinterpret_cast<const f32x4*>(&b.bias[hw][32 * kb + 16 * hh]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 v4 = bp[q4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kb][4 * q4 + e] = v4[e];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = 0.0f;
+      }
+    }
 #pragma unroll
     for (int ks = 0; ks < DK; ++ks)
 #pragma unroll
@@ -318,17 +328,6 @@ attn_bf16_kernel(
             &b.ks[row * D + 8 * ((2 * ks + hh) ^ (row & Smem::SW))]);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      u32x4 ke = u32x4{0, 0, 0, 0};
-      if (hh == 0) {
-        const u32x2 bb = HAS_BIAS ? b.bias[hw][32 * kb + l32] : u32x2{0, 0};
-        ke[0] = bb[0];                     // [bias'_hi, bias'_mid]
-        ke[1] = bb[1];                     // [bias'_lo, 0]
-      }
-      s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ke), qf[DK],
-                                                      s[kb], 0, 0, 0);
-    }
 
     // causal / tail mask (only tiles that reach past a query or past N)
     const bool need_mask = (CAUSAL && k0 + kBK - 1 > pos0) || (k0 + kBK > Ne);
