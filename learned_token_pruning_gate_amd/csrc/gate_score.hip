@@ -329,8 +329,9 @@ constexpr int kLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);    // lgkmcnt(0) on
 
 constexpr int kDepth = 4;               // k-stages in flight in the streaming kernel
 
+template <int RT>
 struct XSlot {
-  u32x4 b[8][64];   // (row tile mt, k half kk) -> block mt*2+kk, lane order
+  u32x4 b[8 * RT][64];   // (row tile mt, k half kk) -> block mt*2+kk, lane order
 };
 
 // Packed W1 (tg_gate_pack_w1): for stage ks = k / 64, column tile ht = n / 16
@@ -353,20 +354,31 @@ __device__ __forceinline__ float silu_fast(float z) {
 // stages are then fully unrolled.  Either way every ring index is a
 // compile-time constant, so the slots are distinct LDS objects and the W1
 // register sets distinct registers: the compiler never merges their waits.
-template <int NTW, int NW, int NST, bool PACKED>
+// RT: 64-row tiles per workgroup.  Each workgroup streams all of W1 through
+// its CU once, so RT = 2 (128 rows) halves W1's traffic per row; its A
+// fragments (twice as many) are read in the stage that uses them rather than
+// one stage ahead, which would not fit the registers.
+template <int NTW, int NW, int NST, bool PACKED, int RT = 1>
 __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     float eps, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
     const float* __restrict__ w2, float b2, float* __restrict__ scores, int32_t T, int32_t d,
     int32_t h, const int32_t* __restrict__ t_dyn) {
-  constexpr int TM = 64;
+  constexpr int TM = 64 * RT;
+  constexpr int MT = 4 * RT;                   // 16-row tiles
   constexpr int DEPTH = kDepth;
   constexpr int R = DEPTH + 1;                 // ring length
-  constexpr int XPW = 8 / NW;                  // residual blocks each wave loads per stage
+  constexpr int XPW = 8 * RT / NW;             // residual blocks each wave loads per stage
   constexpr int PER_STAGE = XPW + 2 * NTW;     // vector-memory instructions per wave per stage
+  constexpr bool AHEAD = RT == 1;              // A fragments read one stage ahead
+  // sum of squares: with 8 waves over 4 row tiles, wave w takes row tile
+  // w & 3, k half w >> 2; otherwise wave w takes row tile w, both halves
+  constexpr bool SS_HALVES = NW == 8 && RT == 1;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(RT == 1 || (RT == 2 && NW == 8), "128-row tiles with 8 waves");
   static_assert(DEPTH >= 2 && R <= 8 && PER_STAGE * (DEPTH - 1) <= 63, "ring shape");
-  __shared__ __attribute__((aligned(16))) XSlot xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7;
+  using XS = XSlot<RT>;
+  __shared__ __attribute__((aligned(16))) XS xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7;
   __shared__ float s_ss[2][TM];
   __shared__ float s_rs[TM];
   __shared__ float s_part[NW][TM];
@@ -422,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   const int rot = static_cast<int>((blockIdx.x >> 3) % static_cast<uint32_t>(nstages));
 
   u32x4 wr[R][NTW][2];   // W1 fragments, one set per ring slot
-  auto issue = [&](int st, XSlot& sl, u32x4 (&w)[NTW][2]) {
+  auto issue = [&](int st, XS& sl, u32x4 (&w)[NTW][2]) {
     int ks = st + rot;
     ks = ks >= nstages ? ks - nstages : ks;
 #pragma unroll
@@ -449,9 +461,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     }
   };
 
-  f32x4 acc[4][NTW];
+  f32x4 acc[MT][NTW];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[m][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // Row sums of squares on the matrix cores: an A fragment times itself
@@ -460,27 +472,59 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   // waves, wave w takes row tile w & 3 and k half w >> 2 of every stage; with
   // 4 waves, wave w takes row tile w and both k halves.
   f32x4 acc_ss = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int ss_tile = NW == 8 ? (wave & 3) : wave;
-  const int ss_half = NW == 8 ? (wave >> 2) : 0;
+  const int ss_tile = SS_HALVES ? (wave & 3) : wave;
+  const int ss_half = SS_HALVES ? (wave >> 2) : 0;
 
   // One stage ahead: stage s's A fragments (and this wave's sum-of-squares
   // fragment) sit in registers, read during stage s-1, so the LDS latency of
   // a stage's reads and the barrier before them overlap the previous stage's
   // MFMAs instead of preceding this stage's.
   u32x4 av[2][4];
-  u32x4 mine[2];   // XPW of them
-  auto read_frags = [&](const XSlot& sl, u32x4 (&a)[2][4], u32x4 (&mn)[2]) {
+  u32x4 mine[2];   // the sum-of-squares fragments (one or both k halves)
+  constexpr int NSS = SS_HALVES ? 1 : 2;
+  auto read_frags = [&](const XS& sl, u32x4 (&a)[2][4], u32x4 (&mn)[2]) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
       for (int m = 0; m < 4; ++m) a[kk][m] = sl.b[m * 2 + kk][lane];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i < XPW) mn[i] = sl.b[ss_tile * 2 + (NW == 8 ? ss_half : i)][lane];
+    for (int i = 0; i < NSS; ++i) mn[i] = sl.b[ss_tile * 2 + (SS_HALVES ? ss_half : i)][lane];
   };
-  auto stage = [&](int s, const XSlot& sl_next, const u32x4 (&wc)[NTW][2], XSlot& nsl,
-                   u32x4 (&wn)[NTW][2]) {
+  auto stage = [&](int s, const XS& sl_cur, const XS& sl_next, const u32x4 (&wc)[NTW][2],
+                   XS& nsl, u32x4 (&wn)[NTW][2]) {
     const int last = nstages - 1;
+    if constexpr (!AHEAD) {
+      // this wave's loads of stage s are done (later stages may be in
+      // flight); after the barrier every wave's stage s has landed and stage
+      // s-1's slot is free for stage s + DEPTH
+      (void)sl_next;
+      wait_own(s + DEPTH - 1 <= last ? DEPTH - 1 : last - s);
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+      if (s + DEPTH <= last) issue(s + DEPTH, nsl, wn);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NSS; ++i) {
+        const u32x4 mn = sl_cur.b[ss_tile * 2 + (SS_HALVES ? ss_half : i)][lane];
+        acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mn),
+                                                         __builtin_bit_cast(bf16x8, mn), acc_ss,
+                                                         0, 0, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          const u32x4 a = sl_cur.b[m * 2 + kk][lane];
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, wc[nt][kk]),
+                acc[m][nt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      return;
+    }
     u32x4 an[2][4];
     u32x4 mn[2];
     if (s < last) {
@@ -496,20 +540,20 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     // keep the reads and the prefetch issued here, ahead of this stage's MFMAs
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i < XPW)
-        acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mine[i]),
-                                                         __builtin_bit_cast(bf16x8, mine[i]),
-                                                         acc_ss, 0, 0, 0);
+    for (int i = 0; i < NSS; ++i)
+      acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mine[i]),
+                                                       __builtin_bit_cast(bf16x8, mine[i]),
+                                                       acc_ss, 0, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-          acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, av[kk][m]), __builtin_bit_cast(bf16x8, wc[nt][kk]),
-              acc[m][nt], 0, 0, 0);
+          if constexpr (AHEAD)
+            acc[m][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, av[kk][m]), __builtin_bit_cast(bf16x8, wc[nt][kk]),
+                acc[m][nt], 0, 0, 0);
     }
     // every MFMA of this stage is issued before the next stage's barrier: a
     // wave waiting there has its matrix work queued behind it
@@ -527,8 +571,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
 #define TG_SLOT(X)                                                                  \
   ((X) == 0 ? xs0 : (X) == 1 ? xs1 : (X) == 2 ? xs2 : (X) == 3 ? xs3 : (X) == 4 ? xs4 \
    : (X) == 5 ? xs5 : (X) == 6 ? xs6 : xs7)
-#define TG_STAGE_SLOT(S, J) \
-  stage((S), TG_SLOT((J + 1) % R), wr[J], TG_SLOT((J + DEPTH) % R), wr[(J + DEPTH) % R])
+#define TG_STAGE_SLOT(S, J)                                                    \
+  stage((S), TG_SLOT(J), TG_SLOT((J + 1) % R), wr[J], TG_SLOT((J + DEPTH) % R), \
+        wr[(J + DEPTH) % R])
   auto run = [&](int s, int j) {   // j == s % R, a constant after unrolling
     switch (j) {
       case 0: TG_STAGE_SLOT(s, 0); break;
@@ -552,9 +597,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   if constexpr (DEPTH > 4) if (4 < nstages) issue(4, xs4, wr[4 % R]);
   if constexpr (DEPTH > 5) if (5 < nstages) issue(5, xs5, wr[5 % R]);
   if constexpr (DEPTH > 6) if (6 < nstages) issue(6, xs6, wr[6 % R]);
-  wait_own(nstages - 1 < DEPTH - 1 ? nstages - 1 : DEPTH - 1);
-  __builtin_amdgcn_s_barrier();
-  read_frags(xs0, av, mine);
+  if constexpr (AHEAD) {
+    wait_own(nstages - 1 < DEPTH - 1 ? nstages - 1 : DEPTH - 1);
+    __builtin_amdgcn_s_barrier();
+    read_frags(xs0, av, mine);
+  }
   if constexpr (NST > 0) {
 #pragma unroll
     for (int s = 0; s < NST; ++s) run(s, s % R);
@@ -573,14 +620,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const float v = r == 0 ? acc_ss[0] : r == 1 ? acc_ss[1] : r == 2 ? acc_ss[2] : acc_ss[3];
     s_ss[ss_half][ss_tile * 16 + (lane & 15)] = v;
   }
-  if (NW == 4 && tid < TM) s_ss[1][tid] = 0.0f;
+  if (!SS_HALVES && tid < TM) s_ss[1][tid] = 0.0f;
   __syncthreads();
   if (tid < TM) s_rs[tid] = 1.0f / sqrtf((s_ss[0][tid] + s_ss[1][tid]) / static_cast<float>(d) + eps);
   __syncthreads();
 
-  float part[4][4];
+  float part[MT][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) part[m][r] = 0.0f;
 #pragma unroll
@@ -589,7 +636,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const float bb = b1 ? b1[n] : 0.0f;
     const float ww = w2[n];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float z = fmaf(acc[m][nt][r], s_rs[m * 16 + lgrp * 4 + r], bb);
@@ -597,7 +644,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
       }
   }
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float v = part[m][r];
@@ -701,27 +748,35 @@ void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint
                                  d, t_dyn);
 }
 
-// Streaming kernel dispatch: h = 16 * NTW * NW.
+// Streaming kernel dispatch: h = 16 * NTW * NW.  At h = 256 a prompt long
+// enough for two rounds of 128-row workgroups on every CU takes 128-row
+// tiles (half the W1 traffic per row); shorter ones keep 64-row tiles, so
+// that every CU still gets a workgroup.
 void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
                    const uint16_t* x, int64_t ld, const uint8_t* p, float eps,
                    const uint16_t* w, const float* b1, const float* w2, float b2, float* out,
                    const int32_t* t_dyn) {
-  const dim3 grid(static_cast<uint32_t>((T + 63) / 64));
   const int32_t T32 = static_cast<int32_t>(T), h32 = static_cast<int32_t>(h);
-#define TG_GATE_STREAM(NTW, NW, NST)                                                         \
+  const bool rows128 = h == 256 && (T + 127) / 128 >= 2 * static_cast<int64_t>(device_cu_count());
+#define TG_GATE_STREAM(NTW, NW, NST, RT)                                                     \
   do {                                                                                      \
+    const dim3 grid(static_cast<uint32_t>((T + 64 * RT - 1) / (64 * RT)));                  \
     if (packed)                                                                             \
-      gate_bf16_stream_kernel<NTW, NW, NST, true><<<grid, dim3(NW * 64), 0, s>>>(           \
+      gate_bf16_stream_kernel<NTW, NW, NST, true, RT><<<grid, dim3(NW * 64), 0, s>>>(       \
           x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
     else                                                                                    \
-      gate_bf16_stream_kernel<NTW, NW, NST, false><<<grid, dim3(NW * 64), 0, s>>>(          \
+      gate_bf16_stream_kernel<NTW, NW, NST, false, RT><<<grid, dim3(NW * 64), 0, s>>>(      \
           x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
   } while (0)
-  if (h == 256 && d == 2048) TG_GATE_STREAM(2, 8, 32);   // Qwen3-1.7B hidden size, h = 256
-  else if (h == 256) TG_GATE_STREAM(2, 8, 0);
-  else if (h == 192) TG_GATE_STREAM(3, 4, 0);
-  else if (h == 128) TG_GATE_STREAM(2, 4, 0);
-  else TG_GATE_STREAM(1, 4, 0);
+  if (h == 256 && d == 2048) {   // Qwen3-1.7B hidden size, h = 256
+    if (rows128) TG_GATE_STREAM(2, 8, 32, 2);
+    else TG_GATE_STREAM(2, 8, 32, 1);
+  } else if (h == 256) {
+    if (rows128) TG_GATE_STREAM(2, 8, 0, 2);
+    else TG_GATE_STREAM(2, 8, 0, 1);
+  } else if (h == 192) TG_GATE_STREAM(3, 4, 0, 1);
+  else if (h == 128) TG_GATE_STREAM(2, 4, 0, 1);
+  else TG_GATE_STREAM(1, 4, 0, 1);
 #undef TG_GATE_STREAM
 }
 

@@ -114,6 +114,22 @@ def test_gate_bf16_stream_cases(T, d, h, with_b1, frac, packed):
                      "gate_bf16_stream_T%d_d%d_h%d_%s" % (T, d, h, "packed" if packed else "rowmajor"))
 
 
+@pytest.mark.parametrize("T,d,with_b1,frac", [
+    (65613, 2048, True, 0.8),   # 128-row tiles, 32-stage kernel, ragged last tile
+    (66000, 1088, False, 0.6),  # 128-row tiles, 17 stages (the ring wraps partway)
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gate_bf16_stream_128_rows(T, d, with_b1, frac, packed):
+    """At h = 256, prompts long enough for two rounds of 128-row workgroups
+    on every CU take 128-row tiles: every row against the oracle."""
+    args = _random_case(T, d, 256, False, with_b1, frac)
+    got = run_gpu(*args, stride_pad=8 if T % 2 else 0, packed=packed)
+    ref = run_oracle(*args)
+    assert np.all(got[args[1] == 0] == 0)
+    assert_close_abs(got, ref, BF16_ABS,
+                     "gate_bf16_stream128_T%d_d%d_%s" % (T, d, "packed" if packed else "rowmajor"))
+
+
 @pytest.mark.parametrize("h,d", [(256, 2048), (64, 128), (192, 320)])
 def test_gate_pack_w1_layout(h, d):
     """The packed W1 is the documented permutation of W1's elements: block

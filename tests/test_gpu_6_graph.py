@@ -197,6 +197,9 @@ BUCKETS = [
     # T > 32768: the multi-workgroup select reads the length at run time too
     (dict(T=40000, d=512, h=128, K=700, Hq=8, Hkv=4, D=64, N_cap=1000, seed=32),
      [(36000, 100, 35900), (33001, 50, 32900)], 0, False),
+    # a capacity long enough for the gate's 128-row tiles
+    (dict(T=66000, d=512, h=256, K=900, Hq=8, Hkv=4, D=64, N_cap=1400, seed=33),
+     [(65900, 100, 65500), (40001, 300, 39801)], 0, False),
 ]
 
 
