@@ -60,10 +60,17 @@ constexpr size_t kHistOff[3] = {0, 2048 * 4, 4096 * 4};
 constexpr size_t kCtrlOff = (4096 + 1024) * 4;
 constexpr size_t kFlagOff = kCtrlOff + 256;
 
+// Tokens per workgroup: at least two sweeps (2048 tokens), so that the
+// digit passes' global histogram atomics and the compaction's look-back
+// chain serve half as many workgroups (measured at 128k tokens: the select
+// took 52 us with 1024-token workgroups, 40 us with these and the windowed
+// look-back); at most kMaxBlocks workgroups.
+constexpr int64_t kMinPerBlock = 2 * kChunk;
+
 __host__ __device__ inline int64_t blocks_for(int64_t T, int64_t* per_block) {
   int64_t pb = (T + kMaxBlocks - 1) / kMaxBlocks;
   pb = ((pb + kChunk - 1) / kChunk) * kChunk;
-  if (pb < kChunk) pb = kChunk;
+  if (pb < kMinPerBlock) pb = kMinPerBlock;
   if (per_block) *per_block = pb;
   return T == 0 ? 1 : (T + pb - 1) / pb;
 }
@@ -271,33 +278,53 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   block_inclusive_scan(ca, s_wave, &tot_a);
   block_inclusive_scan(cb, s_wave, &tot_b);
 
-  // (2) exclusive prefix over earlier workgroups
-  if (threadIdx.x == 0) {
+  // (2) exclusive prefix over earlier workgroups.  Wave 0 reads a window of
+  // 64 predecessors' descriptors per round trip (lane i: workgroup top - i):
+  // the nearest inclusive one ends the walk, and every aggregate before it
+  // is added; a nearer predecessor that has not published yet makes the
+  // wave read the window again.
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
     uint32_t pa = 0, pb = 0;
     if (w == 0) {
-      st_agent(&flags[0], pack_desc(kFlagIncl, tot_a, tot_b));
+      if (lane == 0) st_agent(&flags[0], pack_desc(kFlagIncl, tot_a, tot_b));
     } else {
-      st_agent(&flags[w], pack_desc(kFlagAgg, tot_a, tot_b));
-      int64_t j = static_cast<int64_t>(w) - 1;
+      if (lane == 0) st_agent(&flags[w], pack_desc(kFlagAgg, tot_a, tot_b));
+      int64_t top = static_cast<int64_t>(w) - 1;
       while (true) {
-        const uint64_t dsc = ld_agent(&flags[j]);
+        const int64_t j = top - lane;
+        // before the first workgroup: an inclusive descriptor of zero counts
+        const uint64_t dsc = j >= 0 ? ld_agent(&flags[j]) : pack_desc(kFlagIncl, 0, 0);
         const uint64_t f = dsc & (3ull << 62);
-        if (f == 0) {
+        const uint64_t incl = __ballot(f == kFlagIncl);
+        const uint64_t zero = __ballot(f == 0);
+        const int first_incl = incl ? __builtin_ctzll(incl) : 64;
+        const int first_zero = zero ? __builtin_ctzll(zero) : 64;
+        if (first_zero < first_incl) {
           __builtin_amdgcn_s_sleep(1);
           continue;
         }
-        pa += static_cast<uint32_t>((dsc >> 31) & kMask31);
-        pb += static_cast<uint32_t>(dsc & kMask31);
-        if (f == kFlagIncl) break;
-        --j;
+        uint32_t wa = lane <= first_incl ? static_cast<uint32_t>((dsc >> 31) & kMask31) : 0u;
+        uint32_t wb = lane <= first_incl ? static_cast<uint32_t>(dsc & kMask31) : 0u;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          wa += __shfl_xor(wa, off, 64);
+          wb += __shfl_xor(wb, off, 64);
+        }
+        pa += wa;
+        pb += wb;
+        if (first_incl < 64) break;
+        top -= 64;
       }
-      st_agent(&flags[w], pack_desc(kFlagIncl, pa + tot_a, pb + tot_b));
+      if (lane == 0) st_agent(&flags[w], pack_desc(kFlagIncl, pa + tot_a, pb + tot_b));
     }
-    s_pre_a = pa;
-    s_pre_b = pb;
-    if (w == gridDim.x - 1) {
-      const uint32_t B = pb + tot_b;
-      n_kept[0] = static_cast<int32_t>(pa + tot_a + (B < need ? B : need));
+    if (lane == 0) {
+      s_pre_a = pa;
+      s_pre_b = pb;
+      if (w == gridDim.x - 1) {
+        const uint32_t B = pb + tot_b;
+        n_kept[0] = static_cast<int32_t>(pa + tot_a + (B < need ? B : need));
+      }
     }
   }
   __syncthreads();
