@@ -311,7 +311,7 @@ tg_status tg_bias_attn_fwd_ws(tg_dtype dt, int64_t N, int64_t Hq, int64_t Hkv,
  *   dgain[h]  = sum_{r,c} score_c c_r dZ[h,r,c]   (keys with P = 0 add 0)
  *
  * dt            TG_DTYPE_BF16 only (TG_ERR_UNSUPPORTED otherwise).
- * D             64 or 128 (TG_ERR_UNSUPPORTED otherwise).
+ * D             64, 128 or 256 (TG_ERR_UNSUPPORTED otherwise).
  * q, k, v, key_score, gain, q_scale, softmax_scale, causal
  *               as given to tg_bias_attn_fwd.
  * out, lse      the forward's outputs: out [N][Hq][D] bf16 and lse [Hq][N]

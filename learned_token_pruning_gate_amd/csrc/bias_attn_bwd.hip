@@ -27,6 +27,7 @@
 // bf16 inputs on v_mfma_f32_32x32x16_bf16 with fp32 accumulation; P and dZ
 // are rounded to bf16 only as operands of the dV, dK and dQ products.
 #include <algorithm>
+#include <type_traits>
 
 #include "tg_common.hpp"
 
@@ -182,26 +183,38 @@ __global__ __launch_bounds__(256) void attn_bwd_pre_kernel(const uint16_t* __res
 //   dZ'^T = 2^(y - lse2) (dP^T - Delta) c alpha  -> bf16 B operand
 //   dQ^T += K^T dZ'^T             (K^T staged transposed)
 // ---------------------------------------------------------------------------
+// The row tiles (S^T and dP^T operands, all D dims) and the transposed K
+// tile (dQ^T operand, the DO output dims).  With DO < D (head dim 256) a
+// launch produces the output dims [dof, dof + DO) of dQ and recomputes S
+// and dP over all D; its row tiles are single-buffered (two buffers of them
+// would not fit the LDS) and the next tile's rows are stored once every wave
+// has finished the current tile's S and dP.
 template <int D>
-struct DqSmem {
+struct DqRows {
   RowTile<D> k, v;
-  TrTile<D> kt;
   u32x2 bias[4][kTile];
 };
+template <int DO>
+struct DqTr {
+  TrTile<DO> kt;
+};
 
-template <int D, int HPW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
+template <int D, int DO, int HPW, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
     const float* __restrict__ gain, const float* __restrict__ q_scale, float scale,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, uint16_t* __restrict__ dq, int32_t N, int32_t Hq,
-    int32_t Hkv, int32_t n_pblocks, int32_t n_hgroups) {
+    int32_t Hkv, int32_t n_pblocks, int32_t n_hgroups, int32_t dof) {
   using St = Stage<D>;
+  using So = Stage<DO>;
   constexpr int PB = 32 * (4 / HPW);
   constexpr int DK = D / 16;
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) DqSmem<D> sm[2];
+  constexpr int DB = DO / 32;
+  constexpr int RB = DO == D ? 2 : 1;   // row-tile buffers
+  __shared__ __attribute__((aligned(16))) DqRows<D> rows[RB];
+  __shared__ __attribute__((aligned(16))) DqTr<DO> trs[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
@@ -253,25 +266,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const float bias_gain = (HAS_BIAS && tid < HPW * kTile) ? gain[hg * HPW + tid / kTile] : 0.0f;
   const uint32_t hoff = static_cast<uint32_t>(kvh) * D * 2;
 
-  u32x4 kr[St::RI], vr[St::RI], kp[St::PPT][4];
+  u32x4 kr[St::RI], vr[St::RI], kp[So::PPT][4];
   float sreg = 0.0f;
   auto load_tile = [&](int t) {
     const int k0 = t * kTile;
     St::load_rows(kr, k_rs, kv_row, hoff, k0, tid);
     St::load_rows(vr, v_rs, kv_row, hoff, k0, tid);
-    St::load_pieces(kp, k_rs, kv_row, hoff, k0, tid);
+    So::load_pieces(kp, k_rs, kv_row, hoff + 2u * static_cast<uint32_t>(dof), k0, tid);
     if (HAS_BIAS && tid < HPW * kTile)
       sreg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                            s_rs, 4u * static_cast<uint32_t>(k0 + bias_key), 0, 0));
   };
-  auto store_tile = [&](DqSmem<D>& b) {
+  auto store_rows = [&](DqRows<D>& b) {
     St::store_rows(b.k, kr, tid);
     St::store_rows(b.v, vr, tid);
-    St::store_pieces(b.kt, kp, tid);
     if (HAS_BIAS && tid < HPW * kTile)
       b.bias[tid / kTile][bias_key] =
           bf16_triple(sreg == -INFINITY ? masked_bias : bias_gain * sreg * inv_scale);
   };
+  auto store_tr = [&](DqTr<DO>& b) { So::store_pieces(b.kt, kp, tid); };
 
   f32x16 acc[DB];
 #pragma unroll
@@ -283,10 +296,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const int n_tiles = (row_end + kTile - 1) / kTile;
   const int lim = CAUSAL ? min(my_q, N - 1) : N - 1;
   load_tile(0);
-  store_tile(sm[0]);
+  store_rows(rows[0]);
+  store_tr(trs[0]);
   __syncthreads();
   for (int t = 0; t < n_tiles; ++t) {
-    const DqSmem<D>& b = sm[t & 1];
+    const DqRows<D>& b = rows[RB == 2 ? (t & 1) : 0];
+    const DqTr<DO>& bt = trs[t & 1];
     const int k0 = t * kTile;
     const bool more = t + 1 < n_tiles;
     if (more) load_tile(t + 1);
@@ -318,6 +333,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
       s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ke), qf[DK],
                                                       s[kb], 0, 0, 0);
     }
+    if constexpr (RB == 1) {   // every wave is done with this tile's rows
+      __syncthreads();
+      if (more) store_rows(rows[0]);
+    }
     // weights, masked where the key is past the query or past N; a tile
     // whose last key (k0 + 63) no lane of the wave passes needs no mask
     const int rel = lim - k0 - 4 * hh;   // key k0 + 4hh + c visible iff c <= rel
@@ -344,15 +363,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const u32x4 a4 = *reinterpret_cast<const u32x4*>(
-              &b.kt.a[(32 * db + l32) * TrTile<D>::P + 32 * kb + 16 * hf + 8 * hh]);
+              &bt.kt.a[(32 * db + l32) * TrTile<DO>::P + 32 * kb + 16 * hf + 8 * hh]);
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a4),
                                                             zb[kb][hf], acc[db], 0, 0, 0);
         }
-    if (more) store_tile(sm[(t + 1) & 1]);
+    if (more) {
+      if constexpr (RB == 2) store_rows(rows[(t + 1) & 1]);
+      store_tr(trs[(t + 1) & 1]);
+    }
     __syncthreads();
   }
   if (q_ok) {
-    uint16_t* op = dq + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D;
+    uint16_t* op = dq + static_cast<int64_t>(my_q) * Hq * D + static_cast<int64_t>(head) * D + dof;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -373,14 +395,32 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
 //   P = 2^(y - lse2),  dZ = P (dP - Delta),  A += c dZ (per lane)
 //   dV^T += dO^T P,  dK^T += Q^T (c alpha dZ)
 // ---------------------------------------------------------------------------
+// As in the dQ kernel, a launch with DO < D (head dim 256) produces the
+// output dims [dof, dof + DO) of dK and dV, recomputing S and dP over all D.
+// There the row tiles are single-buffered and filled by direct-to-LDS loads
+// (no registers: the K and V fragments already take half the register
+// file), unpadded with the 16-byte chunk c of row r at c ^ (r & 15) so that
+// 16 rows read at one chunk fall in different banks; the next tile's rows
+// are requested once every wave is done with the current ones, and the
+// transposed tiles and per-query vectors stay double-buffered.  The dscore
+// and dgain partials, the same in every launch, are written by the dof = 0
+// launch.
 template <int D>
-struct DkvSmem {
+struct DkvRows {
   RowTile<D> q, d;
-  TrTile<D> qt, dt;
+};
+template <int D>
+struct DkvRowsSw {
+  static constexpr int SW = (D / 8 < 16 ? D / 8 : 16) - 1;
+  uint16_t q[kTile * D], d[kTile * D];
+};
+template <int DO>
+struct DkvTr {
+  TrTile<DO> qt, dt;
   float ac[kTile], acl[kTile], l2[kTile], dl[kTile];   // acl = ac ln 2
 };
 
-template <int D, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
+template <int D, int DO, bool CAUSAL, bool HAS_BIAS, bool HAS_QSCALE>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const float* __restrict__ key_score,
@@ -388,11 +428,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ dout, const float* __restrict__ lse2,
     const float* __restrict__ delta, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
     float* __restrict__ part_kv, float* __restrict__ part_ds, float* __restrict__ part_dg,
-    int32_t N, int32_t Hq, int32_t Hkv, int32_t nkb, int32_t qchunk) {
+    int32_t N, int32_t Hq, int32_t Hkv, int32_t nkb, int32_t qchunk, int32_t dof) {
   using St = Stage<D>;
+  using So = Stage<DO>;
   constexpr int DK = D / 16;
-  constexpr int DB = D / 32;
-  __shared__ __attribute__((aligned(16))) DkvSmem<D> sm[2];
+  constexpr int DB = DO / 32;
+  constexpr int RB = DO == D ? 2 : 1;   // row-tile buffers
+  using Rows = std::conditional_t<RB == 2, DkvRows<D>, DkvRowsSw<D>>;
+  __shared__ __attribute__((aligned(16))) Rows rows[RB];
+  __shared__ __attribute__((aligned(16))) DkvTr<DO> trs[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
@@ -442,16 +486,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const int t_count = min(qchunk, nq - t_lo);   // query tiles per head
   const int n_iter = G * t_count;
 
-  u32x4 qr[St::RI], dr[St::RI], qp[St::PPT][4], dpc[St::PPT][4];
+  u32x4 qr[St::RI], dr[St::RI], qp[So::PPT][4], dpc[So::PPT][4];
   float vec_ac = 0.0f, vec_l2 = 0.0f, vec_dl = 0.0f;
-  auto load_tile = [&](int it) {
+  auto load_rows = [&](int it) {
     const int h = kvh * G + it / t_count;
     const int q0 = (t_lo + it % t_count) * kTile;
     const uint32_t hoff = static_cast<uint32_t>(h) * D * 2;
     St::load_rows(qr, q_rs, q_row, hoff, q0, tid);
     St::load_rows(dr, d_rs, q_row, hoff, q0, tid);
-    St::load_pieces(qp, q_rs, q_row, hoff, q0, tid);
-    St::load_pieces(dpc, d_rs, q_row, hoff, q0, tid);
+  };
+  auto load_tile = [&](int it) {   // the transposed pieces and the vectors
+    const int h = kvh * G + it / t_count;
+    const int q0 = (t_lo + it % t_count) * kTile;
+    const uint32_t hoff = static_cast<uint32_t>(h) * D * 2;
+    So::load_pieces(qp, q_rs, q_row, hoff + 2u * static_cast<uint32_t>(dof), q0, tid);
+    So::load_pieces(dpc, d_rs, q_row, hoff + 2u * static_cast<uint32_t>(dof), q0, tid);
     if (tid < kTile) {
       const int qi = q0 + tid;
       const bool ok = qi < N;
@@ -460,11 +509,46 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       vec_dl = ok ? delta[static_cast<int64_t>(h) * N + qi] : 0.0f;
     }
   };
-  auto store_tile = [&](DkvSmem<D>& b) {
-    St::store_rows(b.q, qr, tid);
-    St::store_rows(b.d, dr, tid);
-    St::store_pieces(b.qt, qp, tid);
-    St::store_pieces(b.dt, dpc, tid);
+  auto store_rows = [&](Rows& b) {
+    if constexpr (RB == 2) {
+      St::store_rows(b.q, qr, tid);
+      St::store_rows(b.d, dr, tid);
+    }
+  };
+  // single-buffered rows: each wave requests its share of the tile's 1-KB
+  // pieces straight into the LDS; rows past N re-read row N - 1 (valid
+  // memory; those queries have weight 0)
+  auto dma_rows = [&](int it) {
+    if constexpr (RB == 1) {
+      const int h = kvh * G + it / t_count;
+      const int q0 = (t_lo + it % t_count) * kTile;
+      constexpr int PPW = kTile * D * 2 / 1024 / 4;
+      Rows& b = rows[0];
+      // the per-lane offsets are formed here, not kept live across the loop
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+#pragma unroll
+      for (int i = 0; i < PPW; ++i) {
+        const int u = wv * PPW + i;
+        const int byte = u * 1024 + 16 * ln;
+        const int r = byte / (2 * D), c = ((byte % (2 * D)) / 16) ^ (r & Rows::SW);
+        const int64_t off = (static_cast<int64_t>(min(q0 + r, N - 1)) * Hq + h) * D + 8 * c;
+        __builtin_amdgcn_global_load_lds(q + off, (__attribute__((address_space(3))) void*)&b.q[u * 512],
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(dout + off,
+                                         (__attribute__((address_space(3))) void*)&b.d[u * 512], 16, 0, 0);
+      }
+    }
+  };
+  // vmcnt(0), other counters untouched: this wave's direct-to-LDS loads
+  // have landed (each wave then passes the barrier)
+  auto dma_wait = [] {
+    if constexpr (RB == 1) __builtin_amdgcn_s_waitcnt(0x0F70);
+  };
+  auto store_tr = [&](DkvTr<DO>& b) {
+    So::store_pieces(b.qt, qp, tid);
+    So::store_pieces(b.dt, dpc, tid);
     if (tid < kTile) {
       b.ac[tid] = vec_ac;
       b.acl[tid] = vec_ac * kLn2;
@@ -483,12 +567,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   const float a_unit = 1.0f / (scale * kLog2e);   // ac = a_unit^-1 c_r
 
   if (n_iter > 0) {
+    if constexpr (RB == 2) load_rows(0);
+    dma_rows(0);
     load_tile(0);
-    store_tile(sm[0]);
+    store_rows(rows[0]);
+    store_tr(trs[0]);
+    dma_wait();
   }
   __syncthreads();
   for (int it = 0; it < n_iter; ++it) {
-    const DkvSmem<D>& b = sm[it & 1];
+    const Rows& br = rows[RB == 2 ? (it & 1) : 0];
+    const DkvTr<DO>& b = trs[it & 1];
     const int h = kvh * G + it / t_count;
     const int q0 = (t_lo + it % t_count) * kTile;
     const bool more = it + 1 < n_iter;
@@ -502,7 +591,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       }
       kf[DK] = __builtin_bit_cast(bf16x8, kb4);
     }
-    if (more) load_tile(it + 1);
+    if (more) {
+      if constexpr (RB == 2) load_rows(it + 1);
+      load_tile(it + 1);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     f32x16 s[2], dp[2];
@@ -514,15 +606,27 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     for (int ks = 0; ks < DK; ++ks)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        const int off = (32 * qb + l32) * RowTile<D>::P + 8 * hh + 16 * ks;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&b.q.a[off]);
+        bf16x8 qa, da;
+        if constexpr (RB == 2) {
+          const int off = (32 * qb + l32) * RowTile<D>::P + 8 * hh + 16 * ks;
+          qa = *reinterpret_cast<const bf16x8*>(&br.q.a[off]);
+          da = *reinterpret_cast<const bf16x8*>(&br.d.a[off]);
+        } else {
+          const int row = 32 * qb + l32;
+          const int off = row * D + 8 * ((2 * ks + hh) ^ (row & Rows::SW));
+          qa = *reinterpret_cast<const bf16x8*>(&br.q[off]);
+          da = *reinterpret_cast<const bf16x8*>(&br.d[off]);
+        }
         s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], s[qb], 0, 0, 0);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(&b.d.a[off]);
         dp[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[ks], dp[qb], 0, 0, 0);
       }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, kf[DK], s[qb], 0, 0, 0);
+    if constexpr (RB == 1) {   // every wave is done with this tile's rows
+      __syncthreads();
+      if (more) dma_rows(it + 1);
+    }
 
     // element (qb, r) is query q0 + 32 qb + 8 (r / 4) + 4 hh + r % 4 and key
     // my_k; a tile that every key of the wave sees whole needs no mask
@@ -559,7 +663,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const int off = (32 * db + l32) * TrTile<D>::P + 32 * qb + 16 * hf + 8 * hh;
+          const int off = (32 * db + l32) * TrTile<DO>::P + 32 * qb + 16 * hf + 8 * hh;
           const u32x4 da4 = *reinterpret_cast<const u32x4*>(&b.dt.a[off]);
           dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, da4),
                                                             pb[qb][hf], dva[db], 0, 0, 0);
@@ -575,18 +679,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
       float g_part = (k_ok && hh == 0 && s_key != -INFINITY) ? s_key * a_key : 0.0f;
 #pragma unroll
       for (int m = 32; m >= 1; m >>= 1) g_part += __shfl_xor(g_part, m, 64);
-      if (lane == 0) part_dg[(slot * 4 + wave) * G + (h - kvh * G)] = g_part;
+      if (lane == 0 && dof == 0) part_dg[(slot * 4 + wave) * G + (h - kvh * G)] = g_part;
       a_sum = 0.0f;
     }
-    if (more) store_tile(sm[(it + 1) & 1]);
+    if (more) {
+      store_rows(rows[RB == 2 ? ((it + 1) & 1) : 0]);
+      store_tr(trs[(it + 1) & 1]);
+      dma_wait();
+    }
     __syncthreads();
   }
 
   const int key_local = 32 * wave + l32;
-  if (HAS_BIAS && hh == 0) part_ds[slot * kKeysPerWg + key_local] = ds_sum;
+  if (HAS_BIAS && hh == 0 && dof == 0) part_ds[slot * kKeysPerWg + key_local] = ds_sum;
   if (split) {
-    // dK^T, dV^T accumulator entries of this lane: dims 32 db + 8 j + 4 hh .. +3
-    float* pk = part_kv + ((slot * 2) * kKeysPerWg + key_local) * D + 4 * hh;
+    // dK^T, dV^T accumulator entries of this lane: dims dof + 32 db + 8 j + 4 hh .. +3
+    float* pk = part_kv + ((slot * 2) * kKeysPerWg + key_local) * D + dof + 4 * hh;
     float* pv = pk + static_cast<size_t>(kKeysPerWg) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -598,7 +706,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
             f32x4{dva[db][4 * j], dva[db][4 * j + 1], dva[db][4 * j + 2], dva[db][4 * j + 3]};
       }
   } else if (k_ok) {
-    const int64_t off = static_cast<int64_t>(my_k) * Hkv * D + static_cast<int64_t>(kvh) * D;
+    const int64_t off = static_cast<int64_t>(my_k) * Hkv * D + static_cast<int64_t>(kvh) * D + dof;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -751,8 +859,11 @@ struct BwdArgs {
   hipStream_t s;
 };
 
+// Head dim 256: each gradient kernel runs twice, once per 128-dim half of
+// its output (the accumulators of all 256 dims do not fit the registers).
 template <int D, int HPW, bool CAUSAL, bool B, bool QS>
 void launch_bwd(const BwdArgs& a, const BwdWorkspace& w) {
+  constexpr int DO = D > 128 ? 128 : D;
   constexpr int PB = 32 * (4 / HPW);
   const int32_t npb = (a.N + PB - 1) / PB, nhg = a.Hq / HPW;
   const int32_t nkb = w.nkb;
@@ -764,20 +875,22 @@ void launch_bwd(const BwdArgs& a, const BwdWorkspace& w) {
   const int64_t rows = static_cast<int64_t>(a.N) * a.Hq;
   attn_bwd_pre_kernel<D><<<dim3(static_cast<uint32_t>((rows + 255) / 256)), dim3(256), 0, a.s>>>(
       a.out, a.dout, a.lse, delta, lse2, a.N, a.Hq);
-  attn_bwd_dkdv_kernel<D, CAUSAL, B, QS>
-      <<<dim3(static_cast<uint32_t>(w.nchunk * nkb * a.Hkv)), dim3(256), 0, a.s>>>(
-          a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.dout, lse2, delta, a.dk, a.dv, pkv, pds,
-          pdg, a.N, a.Hq, a.Hkv, nkb, w.qchunk);
+  for (int dof = 0; dof < D; dof += DO)
+    attn_bwd_dkdv_kernel<D, DO, CAUSAL, B, QS>
+        <<<dim3(static_cast<uint32_t>(w.nchunk * nkb * a.Hkv)), dim3(256), 0, a.s>>>(
+            a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.dout, lse2, delta, a.dk, a.dv, pkv,
+            pds, pdg, a.N, a.Hq, a.Hkv, nkb, w.qchunk, dof);
   if (w.nchunk > 1) {
     const int64_t n = static_cast<int64_t>(a.N) * a.Hkv * (D / 4);
     attn_bwd_kv_reduce_kernel<D><<<dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
                                    a.s>>>(pkv, a.dk, a.dv, a.N, a.Hkv, nkb, w.qchunk,
                                           CAUSAL ? 1 : 0);
   }
-  attn_bwd_dq_kernel<D, HPW, CAUSAL, B, QS><<<dim3(static_cast<uint32_t>(npb * nhg)), dim3(256),
-                                              0, a.s>>>(a.q, a.k, a.v, a.ks, a.gain, a.qs,
-                                                        a.scale, a.dout, lse2, delta, a.dq, a.N,
-                                                        a.Hq, a.Hkv, npb, nhg);
+  for (int dof = 0; dof < D; dof += DO)
+    attn_bwd_dq_kernel<D, DO, HPW, CAUSAL, B, QS>
+        <<<dim3(static_cast<uint32_t>(npb * nhg)), dim3(256), 0, a.s>>>(
+            a.q, a.k, a.v, a.ks, a.gain, a.qs, a.scale, a.dout, lse2, delta, a.dq, a.N, a.Hq,
+            a.Hkv, npb, nhg, dof);
   if (B) {
     const int32_t nds = (a.N + 255) / 256;
     attn_bwd_reduce_kernel<<<dim3(static_cast<uint32_t>(nds + a.Hq)), dim3(256), 0, a.s>>>(
@@ -805,7 +918,7 @@ void launch_bwd_d(const BwdArgs& a, const BwdWorkspace& w) {
 extern "C" size_t tg_bias_attn_bwd_workspace_size(int64_t N, int64_t Hq, int64_t Hkv,
                                                   int64_t D) {
   if (N < 0 || N > tg::kMaxTokens || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 ||
-      N * Hq > tg::kMaxTokens || (D != 64 && D != 128))
+      N * Hq > tg::kMaxTokens || (D != 64 && D != 128 && D != 256))
     return 0;
   return tg::bwd_workspace(N, Hq, Hkv, D).bytes;
 }
@@ -829,9 +942,9 @@ extern "C" tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
                 (long long)Hq, (long long)Hkv);
   if (dt != TG_DTYPE_BF16)
     return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_bwd: bf16 only");
-  if (D != 64 && D != 128)
-    return fail(TG_ERR_UNSUPPORTED, "tg_bias_attn_bwd: head dim must be 64 or 128 (D=%lld)",
-                (long long)D);
+  if (D != 64 && D != 128 && D != 256)
+    return fail(TG_ERR_UNSUPPORTED,
+                "tg_bias_attn_bwd: head dim must be 64, 128 or 256 (D=%lld)", (long long)D);
   if (N * Hq > kMaxTokens || N * Hq * D * 2 > kMaxTokens)
     return fail(TG_ERR_UNSUPPORTED,
                 "tg_bias_attn_bwd: N * Hq * D * 2 must be < 2^31 (32-bit offsets)");
@@ -877,7 +990,11 @@ extern "C" tg_status tg_bias_attn_bwd(tg_dtype dt, int64_t N, int64_t Hq, int64_
   a.s = as_stream(stream);
   const int64_t G = Hq / Hkv;
   const int hpw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  if (D == 128) {
+  if (D == 256) {
+    if (hpw == 4) launch_bwd_d<256, 4>(a, w);
+    else if (hpw == 2) launch_bwd_d<256, 2>(a, w);
+    else launch_bwd_d<256, 1>(a, w);
+  } else if (D == 128) {
     if (hpw == 4) launch_bwd_d<128, 4>(a, w);
     else if (hpw == 2) launch_bwd_d<128, 2>(a, w);
     else launch_bwd_d<128, 1>(a, w);

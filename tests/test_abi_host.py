@@ -269,13 +269,21 @@ def test_attn_bwd_workspace_size(lib):
         (2 * 16 * 2512 + slots * 128 + slots * 4 * 2 + slots * 2 * 128 * 128) * 4
     assert lib.tg_bias_attn_bwd_workspace_size(0, 16, 8, 128) == 0
     assert lib.tg_bias_attn_bwd_workspace_size(100, 6, 4, 128) == 0   # Hq % Hkv != 0
-    assert lib.tg_bias_attn_bwd_workspace_size(100, 8, 4, 256) == 0   # head dim 256
+    # head dim 256: the same layout with [slot][2][128][256] dK/dV partials
+    # (N = 1000, 4/2 heads: 8 key blocks x 2 KV heads = 16 workgroups, split
+    # 8 ways into chunks of 2 of the 16 query tiles: 128 slots)
+    slots = 8 * 8 * 2
+    assert lib.tg_bias_attn_bwd_workspace_size(1000, 4, 2, 256) == \
+        (2 * 4 * 1000 + slots * 128 + slots * 4 * 2 + slots * 2 * 128 * 256) * 4
+    assert lib.tg_bias_attn_bwd_workspace_size(100, 8, 4, 96) == 0    # head dim 96
+    assert lib.tg_bias_attn_bwd_workspace_size(100, 8, 4, 512) == 0   # head dim 512
 
 
 def test_attn_bwd_validation(lib):
     assert _bwd(lib, dt=3) == INVAL
     assert _bwd(lib, dt=F32) == UNSUP
-    assert _bwd(lib, D=256) == UNSUP
+    assert _bwd(lib, D=96) == UNSUP
+    assert _bwd(lib, D=512) == UNSUP
     assert _bwd(lib, Hq=6, Hkv=4) == INVAL
     assert _bwd(lib, ws=None, nbytes=0) == WS
     assert _bwd(lib, nbytes=16) == WS
