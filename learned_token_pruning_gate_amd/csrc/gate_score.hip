@@ -355,9 +355,11 @@ __device__ __forceinline__ float silu_fast(float z) {
 // compile-time constant, so the slots are distinct LDS objects and the W1
 // register sets distinct registers: the compiler never merges their waits.
 // RT: 64-row tiles per workgroup.  Each workgroup streams all of W1 through
-// its CU once, so RT = 2 (128 rows) halves W1's traffic per row; its A
-// fragments (twice as many) are read in the stage that uses them rather than
-// one stage ahead, which would not fit the registers.
+// its CU once, so RT = 2 (128 rows) halves W1's traffic per row and RT = 4
+// (256 rows) quarters it, with 2 or 4 times the matrix work per stage and
+// barrier; their A fragments are read in the stage that uses them rather
+// than one stage ahead, which would not fit the registers.  At RT = 4 a
+// stage's residual slot is 32 KiB, so three stages are in flight, not four.
 template <int NTW, int NW, int NST, bool PACKED, int RT = 1>
 __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
@@ -366,7 +368,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     int32_t h, const int32_t* __restrict__ t_dyn) {
   constexpr int TM = 64 * RT;
   constexpr int MT = 4 * RT;                   // 16-row tiles
-  constexpr int DEPTH = kDepth;
+  constexpr int DEPTH = RT == 4 ? 2 : kDepth;
   constexpr int R = DEPTH + 1;                 // ring length
   constexpr int XPW = 8 * RT / NW;             // residual blocks each wave loads per stage
   constexpr int PER_STAGE = XPW + 2 * NTW;     // vector-memory instructions per wave per stage
@@ -375,7 +377,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   // w & 3, k half w >> 2; otherwise wave w takes row tile w, both halves
   constexpr bool SS_HALVES = NW == 8 && RT == 1;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static_assert(RT == 1 || (RT == 2 && NW == 8), "128-row tiles with 8 waves");
+  static_assert(RT == 1 || ((RT == 2 || RT == 4) && NW == 8), "128/256-row tiles with 8 waves");
   static_assert(DEPTH >= 2 && R <= 8 && PER_STAGE * (DEPTH - 1) <= 63, "ring shape");
   using XS = XSlot<RT>;
   __shared__ __attribute__((aligned(16))) XS xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7;
@@ -406,7 +408,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
 
   // residual blocks wave*XPW + i: row tile (block >> 1), k half (block & 1).
   // Rows past T re-read row T-1 (valid memory); their scores are never stored.
-  const uint16_t* xsrc[2];   // XPW <= 2 (a fixed size: the direct-load builtin rejects a dependent type)
+  const uint16_t* xsrc[4];   // XPW <= 4 (a fixed size: the direct-load builtin rejects a dependent type)
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
     const int blk = wave * XPW + i;
@@ -471,7 +473,11 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   // products of bf16 values are exact in fp32, as on the vector ALUs.  With 8
   // waves, wave w takes row tile w & 3 and k half w >> 2 of every stage; with
   // 4 waves, wave w takes row tile w and both k halves.
-  f32x4 acc_ss = f32x4{0.f, 0.f, 0.f, 0.f};
+  // (256-row tiles: wave w takes row tiles w and w + 8.)
+  constexpr int SST = SS_HALVES ? 1 : MT / NW;   // sum-of-squares row tiles per wave
+  f32x4 acc_ss[SST];
+#pragma unroll
+  for (int j = 0; j < SST; ++j) acc_ss[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ss_tile = SS_HALVES ? (wave & 3) : wave;
   const int ss_half = SS_HALVES ? (wave >> 2) : 0;
 
@@ -504,12 +510,14 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
       if (s + DEPTH <= last) issue(s + DEPTH, nsl, wn);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < NSS; ++i) {
-        const u32x4 mn = sl_cur.b[ss_tile * 2 + (SS_HALVES ? ss_half : i)][lane];
-        acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mn),
-                                                         __builtin_bit_cast(bf16x8, mn), acc_ss,
-                                                         0, 0, 0);
-      }
+      for (int j = 0; j < SST; ++j)
+#pragma unroll
+        for (int i = 0; i < NSS; ++i) {
+          const u32x4 mn = sl_cur.b[(ss_tile + j * NW) * 2 + (SS_HALVES ? ss_half : i)][lane];
+          acc_ss[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mn),
+                                                              __builtin_bit_cast(bf16x8, mn),
+                                                              acc_ss[j], 0, 0, 0);
+        }
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -541,9 +549,9 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NSS; ++i)
-      acc_ss = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mine[i]),
-                                                       __builtin_bit_cast(bf16x8, mine[i]),
-                                                       acc_ss, 0, 0, 0);
+      acc_ss[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, mine[i]),
+                                                          __builtin_bit_cast(bf16x8, mine[i]),
+                                                          acc_ss[0], 0, 0, 0);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
@@ -617,8 +625,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
   // diagonal entry of row i is lane 16 (i >> 2) + i, register i & 3
   if (((lane & 15) >> 2) == lgrp) {
     const int r = lane & 3;
-    const float v = r == 0 ? acc_ss[0] : r == 1 ? acc_ss[1] : r == 2 ? acc_ss[2] : acc_ss[3];
-    s_ss[ss_half][ss_tile * 16 + (lane & 15)] = v;
+#pragma unroll
+    for (int j = 0; j < SST; ++j) {
+      const f32x4 a = acc_ss[j];
+      const float v = r == 0 ? a[0] : r == 1 ? a[1] : r == 2 ? a[2] : a[3];
+      s_ss[ss_half][(ss_tile + j * NW) * 16 + (lane & 15)] = v;
+    }
   }
   if (!SS_HALVES && tid < TM) s_ss[1][tid] = 0.0f;
   __syncthreads();
@@ -749,15 +761,17 @@ void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint
 }
 
 // Streaming kernel dispatch: h = 16 * NTW * NW.  At h = 256 a prompt long
-// enough for two rounds of 128-row workgroups on every CU takes 128-row
-// tiles (half the W1 traffic per row); shorter ones keep 64-row tiles, so
-// that every CU still gets a workgroup.
+// enough for two rounds of 256-row (or 128-row) workgroups on every CU takes
+// those tiles (a quarter or half of the W1 traffic per row); shorter ones
+// keep 64-row tiles, so that every CU still gets a workgroup.
 void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
                    const uint16_t* x, int64_t ld, const uint8_t* p, float eps,
                    const uint16_t* w, const float* b1, const float* w2, float b2, float* out,
                    const int32_t* t_dyn) {
   const int32_t T32 = static_cast<int32_t>(T), h32 = static_cast<int32_t>(h);
-  const bool rows128 = h == 256 && (T + 127) / 128 >= 2 * static_cast<int64_t>(device_cu_count());
+  const int64_t cus = device_cu_count();
+  const bool rows256 = h == 256 && (T + 255) / 256 >= 2 * cus;
+  const bool rows128 = h == 256 && (T + 127) / 128 >= 2 * cus;
 #define TG_GATE_STREAM(NTW, NW, NST, RT)                                                     \
   do {                                                                                      \
     const dim3 grid(static_cast<uint32_t>((T + 64 * RT - 1) / (64 * RT)));                  \
@@ -769,10 +783,12 @@ void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
           x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
   } while (0)
   if (h == 256 && d == 2048) {   // Qwen3-1.7B hidden size, h = 256
-    if (rows128) TG_GATE_STREAM(2, 8, 32, 2);
+    if (rows256) TG_GATE_STREAM(2, 8, 32, 4);
+    else if (rows128) TG_GATE_STREAM(2, 8, 32, 2);
     else TG_GATE_STREAM(2, 8, 32, 1);
   } else if (h == 256) {
-    if (rows128) TG_GATE_STREAM(2, 8, 0, 2);
+    if (rows256) TG_GATE_STREAM(2, 8, 0, 4);
+    else if (rows128) TG_GATE_STREAM(2, 8, 0, 2);
     else TG_GATE_STREAM(2, 8, 0, 1);
   } else if (h == 192) TG_GATE_STREAM(3, 4, 0, 1);
   else if (h == 128) TG_GATE_STREAM(2, 4, 0, 1);

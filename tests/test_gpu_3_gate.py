@@ -130,6 +130,32 @@ def test_gate_bf16_stream_128_rows(T, d, with_b1, frac, packed):
                      "gate_bf16_stream128_T%d_d%d_%s" % (T, d, "packed" if packed else "rowmajor"))
 
 
+@pytest.mark.parametrize("T,d,with_b1,frac", [
+    (131172, 2048, True, 0.8),   # 256-row tiles, 32-stage kernel, ragged last tile
+    (140001, 1088, False, 0.6),  # 256-row tiles, 17 stages (the ring wraps partway)
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gate_bf16_stream_256_rows(T, d, with_b1, frac, packed):
+    """At h = 256, prompts long enough for two rounds of 256-row workgroups
+    on every CU take 256-row tiles: against the oracle on the first and last
+    rows, the rows at every tenth workgroup boundary and random rows."""
+    args = _random_case(T, d, 256, False, with_b1, frac)
+    resid, prunable, w1, w2, b2, gamma, b1, eps, dt = args
+    got = run_gpu(*args, stride_pad=8 if T % 2 else 0, packed=packed)
+    rng = np.random.default_rng(T + d)
+    edges = np.arange(0, T, 2560)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 300), np.arange(T - 300, T), edges, np.minimum(edges + 255, T - 1),
+        rng.choice(T, size=2000, replace=False)]))
+    sub = np.zeros(T, np.uint8)
+    sub[rows] = prunable[rows]
+    ref = run_oracle(resid[rows], sub[rows], w1, w2, b2, gamma, b1, eps, dt)
+    assert np.all(got[prunable == 0] == 0)
+    assert np.count_nonzero(got) <= int(prunable.sum())
+    assert_close_abs(got[rows], ref, BF16_ABS,
+                     "gate_bf16_stream256_T%d_d%d_%s" % (T, d, "packed" if packed else "rowmajor"))
+
+
 @pytest.mark.parametrize("h,d", [(256, 2048), (64, 128), (192, 320)])
 def test_gate_pack_w1_layout(h, d):
     """The packed W1 is the documented permutation of W1's elements: block
