@@ -459,6 +459,7 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t histc[NCOPY > 1 ? 2048 * NCOPY : 4];
   __shared__ uint32_t s_wave[2 * (kOneThreads / 64)];
   __shared__ uint32_t s_state2[2][4];   // prefix, mask, need, resolved
+  __shared__ uint32_t s_np[kOneThreads / 64];   // prunable tokens per wave
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
@@ -474,6 +475,7 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
       const_cast<uint8_t*>(prunable), 0, T, 0x00020000);
   const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(scores), 0, T * 4, 0x00020000);
+  uint32_t np = 0;   // this thread's prunable tokens
   for (int base = 0; base < T; base += kOneThreads * 16) {
     const int t0 = base + tid * 16;
     if (t0 < T) {
@@ -494,16 +496,28 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
         for (int e = 0; e < 4; ++e) {
           const bool p = ((pm[j] >> (8 * e)) & 0xffu) != 0;
           kv[e] = p ? score_key(__uint_as_float(sv[j][e])) + 1u : 0u;
+          np += p;
         }
         // t0 + 15 < MAXT: t0 is a multiple of 16 below T <= MAXT
         *reinterpret_cast<u32x4*>(&keys[t0 + 4 * j]) = kv;
       }
     }
   }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) np += __shfl_xor(np, off, 64);
+  if (lane == 0) s_np[tid >> 6] = np;
   __syncthreads();
+  uint32_t n_p = 0;   // |P|
+#pragma unroll
+  for (int w = 0; w < kOneThreads / 64; ++w) n_p += s_np[w];
 
-  // threshold: up to three digit passes; wave 0 resolves each digit
-  uint32_t prefix = 0, mask = 0, need = K;
+  // threshold: up to three digit passes; wave 0 resolves each digit.  Keep
+  // all or none of the prunable tokens (K >= |P| or K == 0): no digit to
+  // resolve (prefix and mask 0 make every prunable token tie at the
+  // threshold, and need says how many of them stay).
+  const bool all_or_none = K >= n_p || K == 0;
+  uint32_t prefix = 0, mask = 0, need = all_or_none ? (K >= n_p ? n_p : 0u) : K;
+  if (!all_or_none) {
 #pragma unroll
   for (int pass = 0; pass < 3; ++pass) {
     const int bits = pass == 2 ? 10 : 11;
@@ -598,6 +612,7 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
     const bool resolved = s_state[3] != 0;
     // no second barrier: the next pass writes the other histogram and state
     if (resolved) break;   // uniform across the workgroup
+  }
   }
 
   // ordered compaction: thread tid owns the contiguous tokens
