@@ -519,100 +519,101 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
   uint32_t prefix = 0, mask = 0, need = all_or_none ? (K >= n_p ? n_p : 0u) : K;
   if (!all_or_none) {
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    const int bits = pass == 2 ? 10 : 11;
-    const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
-    const uint32_t nb = 1u << bits;
-    uint32_t* hist = hist2[pass & 1];
-    uint32_t* s_state = s_state2[pass & 1];
-    // thread tid takes keys 4 tid + 4096 i .. + 3 with 16-byte LDS reads
-    // (staged keys past T, up to the next multiple of 16, are 0: skipped)
+    for (int pass = 0; pass < 3; ++pass) {
+      const int bits = pass == 2 ? 10 : 11;
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t nb = 1u << bits;
+      uint32_t* hist = hist2[pass & 1];
+      uint32_t* s_state = s_state2[pass & 1];
+      // thread tid takes keys 4 tid + 4096 i .. + 3 with 16-byte LDS reads
+      // (staged keys past T, up to the next multiple of 16, are 0: skipped)
 #pragma unroll
-    for (int i = 0; i < MAXT / (4 * kOneThreads); ++i) {
-      const int t = 4 * tid + 4 * kOneThreads * i;
-      if (t < T) {
-        const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[t]);
+      for (int i = 0; i < MAXT / (4 * kOneThreads); ++i) {
+        const int t = 4 * tid + 4 * kOneThreads * i;
+        if (t < T) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[t]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t k = kv[e];
-          if (k != 0 && (k & mask) == prefix) {
-            const uint32_t bin = (k >> shift) & (nb - 1);
-            if (NCOPY > 1 && pass == 0)
-              atomicAdd(&histc[bin * NCOPY + (lane & (NCOPY - 1))], 1u);
-            else
-              atomicAdd(&hist[bin], 1u);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t k = kv[e];
+            if (k != 0 && (k & mask) == prefix) {
+              const uint32_t bin = (k >> shift) & (nb - 1);
+              if (NCOPY > 1 && pass == 0)
+                atomicAdd(&histc[bin * NCOPY + (lane & (NCOPY - 1))], 1u);
+              else
+                atomicAdd(&hist[bin], 1u);
+            }
           }
         }
-      }
-    }
-    __syncthreads();
-    if (NCOPY > 1 && pass == 0) {   // fold the copies into hist
-      for (int b = tid; b < 2048; b += kOneThreads) {
-        uint32_t c = 0;
-#pragma unroll
-        for (int j = 0; j < NCOPY; j += 4) {
-          const u32x4 v4 = *reinterpret_cast<const u32x4*>(&histc[b * NCOPY + j]);
-          c += v4[0] + v4[1] + v4[2] + v4[3];
-        }
-        hist[b] = c;
       }
       __syncthreads();
-    }
-    if (tid >= 64 && pass < 2) {   // the next pass's histogram (used two passes ago)
-      const uint32_t nb_next = pass == 1 ? 1024u : 2048u;
-      for (uint32_t b = tid - 64; b < nb_next; b += kOneThreads - 64) hist2[(pass + 1) & 1][b] = 0;
-    }
-    if (tid < 64) {
-      // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys),
-      // kept in registers for the search below
-      const int bpl = static_cast<int>(nb) / 64;
-      const int top = static_cast<int>(nb) - 1 - lane * bpl;
-      uint32_t cnt[32];
-      uint32_t mine = 0;
+      if (NCOPY > 1 && pass == 0) {   // fold the copies into hist
+        for (int b = tid; b < 2048; b += kOneThreads) {
+          uint32_t c = 0;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        cnt[j] = j < bpl ? hist[top - j] : 0u;
-        mine += cnt[j];
-      }
-      const uint32_t incl = wave_inclusive_scan(mine);
-      const uint32_t total = __shfl(incl, 63, 64);
-      uint32_t nd = need;
-      if (pass == 0) {   // total = |P|: every prunable key matches the empty prefix
-        if (K >= total || K == 0) {
-          if (lane == 0) {
-            s_state[0] = 0;
-            s_state[1] = 0;
-            s_state[2] = K >= total ? total : 0u;
-            s_state[3] = 1;
+          for (int j = 0; j < NCOPY; j += 4) {
+            const u32x4 v4 = *reinterpret_cast<const u32x4*>(&histc[b * NCOPY + j]);
+            c += v4[0] + v4[1] + v4[2] + v4[3];
           }
-          nd = 0;   // no lane resolves a digit
+          hist[b] = c;
         }
+        __syncthreads();
       }
-      const uint32_t above = incl - mine;
-      if (nd != 0 && above < nd && nd <= above + mine) {
-        // the one bin where the running count first reaches nd
-        uint32_t cum = above;
+      if (tid >= 64 && pass < 2) {   // the next pass's histogram (used two passes ago)
+        const uint32_t nb_next = pass == 1 ? 1024u : 2048u;
+        for (uint32_t b = tid - 64; b < nb_next; b += kOneThreads - 64)
+          hist2[(pass + 1) & 1][b] = 0;
+      }
+      if (tid < 64) {
+        // lane l owns bins nb-1-l*bpl down to nb-(l+1)*bpl (descending keys),
+        // kept in registers for the search below
+        const int bpl = static_cast<int>(nb) / 64;
+        const int top = static_cast<int>(nb) - 1 - lane * bpl;
+        uint32_t cnt[32];
+        uint32_t mine = 0;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-          const uint32_t c = cnt[j];
-          if (cum < nd && cum + c >= nd) {
-            s_state[0] = prefix | (static_cast<uint32_t>(top - j) << shift);
-            s_state[1] = mask | ((nb - 1) << shift);
-            s_state[2] = nd - cum;
-            s_state[3] = (nd - cum == c || pass == 2) ? 1u : 0u;
+          cnt[j] = j < bpl ? hist[top - j] : 0u;
+          mine += cnt[j];
+        }
+        const uint32_t incl = wave_inclusive_scan(mine);
+        const uint32_t total = __shfl(incl, 63, 64);
+        uint32_t nd = need;
+        if (pass == 0) {   // total = |P|: every prunable key matches the empty prefix
+          if (K >= total || K == 0) {
+            if (lane == 0) {
+              s_state[0] = 0;
+              s_state[1] = 0;
+              s_state[2] = K >= total ? total : 0u;
+              s_state[3] = 1;
+            }
+            nd = 0;   // no lane resolves a digit
           }
-          cum += c;
+        }
+        const uint32_t above = incl - mine;
+        if (nd != 0 && above < nd && nd <= above + mine) {
+          // the one bin where the running count first reaches nd
+          uint32_t cum = above;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t c = cnt[j];
+            if (cum < nd && cum + c >= nd) {
+              s_state[0] = prefix | (static_cast<uint32_t>(top - j) << shift);
+              s_state[1] = mask | ((nb - 1) << shift);
+              s_state[2] = nd - cum;
+              s_state[3] = (nd - cum == c || pass == 2) ? 1u : 0u;
+            }
+            cum += c;
+          }
         }
       }
+      __syncthreads();
+      prefix = s_state[0];
+      mask = s_state[1];
+      need = s_state[2];
+      const bool resolved = s_state[3] != 0;
+      // no second barrier: the next pass writes the other histogram and state
+      if (resolved) break;   // uniform across the workgroup
     }
-    __syncthreads();
-    prefix = s_state[0];
-    mask = s_state[1];
-    need = s_state[2];
-    const bool resolved = s_state[3] != 0;
-    // no second barrier: the next pass writes the other histogram and state
-    if (resolved) break;   // uniform across the workgroup
-  }
   }
 
   // ordered compaction: thread tid owns the contiguous tokens
