@@ -141,14 +141,15 @@ def test_attn_bwd_invariants_and_determinism(D):
     assert abs(tot) <= 1e-3 * float(ds1.double().abs().sum()), tot
 
 
-def test_attn_bwd_t16k_full():
-    """The 16k prompt's kept set (N = 2512, 16/8 heads, D = 128): every
-    gradient element against the oracle."""
-    w = workloads.get("t16k")
+@pytest.mark.parametrize("name", ["t16k", "t16k-d256"])
+def test_attn_bwd_t16k_full(name):
+    """The 16k prompt's kept set (N = 2512; 16/8 heads at D = 128, 8/2 heads
+    at D = 256): every gradient element against the oracle."""
+    w = workloads.get(name)
     _, a = workloads.generate(w)
     rng = np.random.default_rng(93)
     s = rng.standard_normal(w.n_kept).astype(np.float32)
     do = workloads.to_bf16_bits(rng.standard_normal(a.q.shape).astype(np.float32))
     got = gpu_bwd(a.q, a.k, a.v, do, s, a.gain, None)
     ref = ref_bwd(a.q, a.k, a.v, do, s, a.gain, None)
-    check(got, ref, "attn_bwd_t16k_full")
+    check(got, ref, "attn_bwd_full_" + name)
