@@ -84,6 +84,32 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// A thread's 4 consecutive tokens l0 .. l0 + 3 of its workgroup's range
+// [begin, begin + nloc): the prunable bytes as one word and the scores as
+// one 16-byte load, through buffer resources based at the range (reads past
+// it return 0), so that both are in flight together.  The range check is
+// per dword, so the thread whose 4 tokens straddle the range's end reads its
+// prunable bytes singly (tail_fix).
+struct Tok4 {
+  uint32_t p;   // byte e: token l0 + e is prunable (nonzero) or not
+  u32x4 s;      // score bits of the 4 tokens
+};
+__device__ __forceinline__ Tok4 load_tok4(__amdgpu_buffer_rsrc_t p_rs,
+                                          __amdgpu_buffer_rsrc_t s_rs, int32_t l0) {
+  Tok4 r;
+  r.p = __builtin_amdgcn_raw_buffer_load_b32(p_rs, l0, 0, 0);
+  r.s = __builtin_amdgcn_raw_buffer_load_b128(s_rs, 4 * l0, 0, 0);
+  return r;
+}
+__device__ __forceinline__ uint32_t tail_fix(uint32_t p, const uint8_t* __restrict__ pb,
+                                             int32_t l0, int32_t nloc) {
+  if (l0 + 4 <= nloc) return p;
+  uint32_t q = 0;
+  for (int e = 0; e < 4; ++e)
+    if (l0 + e < nloc) q |= static_cast<uint32_t>(pb[l0 + e] != 0) << (8 * e);
+  return q;
+}
+
 // Inclusive block-wide sum scan (256 threads) of one u32 per thread.
 __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* s_wave,
                                                          uint32_t* total) {
@@ -149,14 +175,27 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(
 
   const int64_t begin = static_cast<int64_t>(blockIdx.x) * per_block;
   const int64_t end = begin + per_block < T ? begin + per_block : T;
-  for (int64_t base = begin; base < end; base += kChunk) {
-    const int64_t t0 = base + static_cast<int64_t>(threadIdx.x) * kItems;
+  const int32_t nloc = end > begin ? static_cast<int32_t>(end - begin) : 0;
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(prunable + begin), 0, nloc, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scores + begin), 0, 4 * nloc, 0x00020000);
+  // two sweeps' loads in flight per round trip
+  for (int32_t lb = 0; lb < nloc; lb += 2 * kChunk) {
+    Tok4 tk[2];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int64_t t = t0 + i;
-      if (t < end && prunable[t]) {
-        const uint32_t key = score_key(scores[t]);
-        if ((key & mask) == prefix) atomicAdd(&h[(key >> SHIFT) & (NB - 1)], 1u);
+    for (int j = 0; j < 2; ++j)
+      tk[j] = load_tok4(p_rs, s_rs, lb + j * kChunk + kItems * static_cast<int32_t>(threadIdx.x));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int32_t l0 = lb + j * kChunk + kItems * static_cast<int32_t>(threadIdx.x);
+      const uint32_t pw = tail_fix(tk[j].p, prunable + begin, l0, nloc);
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        if ((pw >> (8 * i)) & 0xffu) {
+          const uint32_t key = score_key(__uint_as_float(tk[j].s[i]));
+          if ((key & mask) == prefix) atomicAdd(&h[(key >> SHIFT) & (NB - 1)], 1u);
+        }
       }
     }
   }
@@ -255,22 +294,43 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   const uint32_t w = s_ticket;
   const int64_t begin = static_cast<int64_t>(w) * per_block;
   const int64_t end = begin + per_block < T ? begin + per_block : T;
+  const int32_t nloc = end > begin ? static_cast<int32_t>(end - begin) : 0;
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(prunable + begin), 0, nloc, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scores + begin), 0, 4 * nloc, 0x00020000);
+  // token l0 + i of a sweep: kept always (a), or tied at the threshold (b)
+  auto classify = [&](const Tok4& tk, uint32_t pw, int32_t l0, int i, uint32_t& fa,
+                      uint32_t& fb) {
+    fa = fb = 0;
+    if (l0 + i < nloc) {
+      if (((pw >> (8 * i)) & 0xffu) == 0) {
+        fa = 1;
+      } else {
+        const uint32_t km = score_key(__uint_as_float(tk.s[i])) & mask;
+        fa = km > prefix;
+        fb = km == prefix;
+      }
+    }
+  };
 
-  // (1) this workgroup's counts of a and b
+  // (1) this workgroup's counts of a and b (two sweeps' loads per round trip)
   uint32_t ca = 0, cb = 0;
-  for (int64_t base = begin; base < end; base += kChunk) {
-    const int64_t t0 = base + static_cast<int64_t>(threadIdx.x) * kItems;
+  for (int32_t lb = 0; lb < nloc; lb += 2 * kChunk) {
+    Tok4 tk[2];
 #pragma unroll
-    for (int i = 0; i < kItems; ++i) {
-      const int64_t t = t0 + i;
-      if (t < end) {
-        if (!prunable[t]) {
-          ++ca;
-        } else {
-          const uint32_t km = score_key(scores[t]) & mask;
-          ca += km > prefix;
-          cb += km == prefix;
-        }
+    for (int j = 0; j < 2; ++j)
+      tk[j] = load_tok4(p_rs, s_rs, lb + j * kChunk + kItems * static_cast<int32_t>(threadIdx.x));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int32_t l0 = lb + j * kChunk + kItems * static_cast<int32_t>(threadIdx.x);
+      const uint32_t pw = tail_fix(tk[j].p, prunable + begin, l0, nloc);
+#pragma unroll
+      for (int i = 0; i < kItems; ++i) {
+        uint32_t fa, fb;
+        classify(tk[j], pw, l0, i, fa, fb);
+        ca += fa;
+        cb += fb;
       }
     }
   }
@@ -331,23 +391,16 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
   uint32_t run_a = s_pre_a, run_b = s_pre_b;
 
   // (3) scatter kept token indices in order
-  for (int64_t base = begin; base < end; base += kChunk) {
-    const int64_t t0 = base + static_cast<int64_t>(threadIdx.x) * kItems;
-    uint8_t fa[kItems], fb[kItems];
+  for (int32_t base = 0; base < nloc; base += kChunk) {
+    const int32_t l0 = base + kItems * static_cast<int32_t>(threadIdx.x);
+    const int64_t t0 = begin + l0;
+    const Tok4 tk = load_tok4(p_rs, s_rs, l0);
+    const uint32_t pw = tail_fix(tk.p, prunable + begin, l0, nloc);
+    uint32_t fa[kItems], fb[kItems];
     uint32_t la = 0, lb = 0;
 #pragma unroll
     for (int i = 0; i < kItems; ++i) {
-      const int64_t t = t0 + i;
-      fa[i] = fb[i] = 0;
-      if (t < end) {
-        if (!prunable[t]) {
-          fa[i] = 1;
-        } else {
-          const uint32_t km = score_key(scores[t]) & mask;
-          fa[i] = km > prefix;
-          fb[i] = km == prefix;
-        }
-      }
+      classify(tk, pw, l0, i, fa[i], fb[i]);
       la += fa[i];
       lb += fb[i];
     }
@@ -503,19 +556,27 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
       }
     }
   }
+  // |P| is summed only when K could reach it (K >= T / 2, or K == 0)
+  const bool count_p = K == 0 || 2 * static_cast<int64_t>(K) >= T;
+  if (count_p) {
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) np += __shfl_xor(np, off, 64);
-  if (lane == 0) s_np[tid >> 6] = np;
+    for (int off = 32; off >= 1; off >>= 1) np += __shfl_xor(np, off, 64);
+    if (lane == 0) s_np[tid >> 6] = np;
+  }
   __syncthreads();
-  uint32_t n_p = 0;   // |P|
+  uint32_t n_p = 0xffffffffu;   // |P|, or "unknown"
+  if (count_p) {
+    n_p = 0;
 #pragma unroll
-  for (int w = 0; w < kOneThreads / 64; ++w) n_p += s_np[w];
+    for (int w = 0; w < kOneThreads / 64; ++w) n_p += s_np[w];
+  }
 
   // threshold: up to three digit passes; wave 0 resolves each digit.  Keep
   // all or none of the prunable tokens (K >= |P| or K == 0): no digit to
   // resolve (prefix and mask 0 make every prunable token tie at the
-  // threshold, and need says how many of them stay).
-  const bool all_or_none = K >= n_p || K == 0;
+  // threshold, and need says how many of them stay).  Otherwise the first
+  // pass finds |P| and still decides this case.
+  const bool all_or_none = count_p && (K >= n_p || K == 0);
   uint32_t prefix = 0, mask = 0, need = all_or_none ? (K >= n_p ? n_p : 0u) : K;
   if (!all_or_none) {
 #pragma unroll
