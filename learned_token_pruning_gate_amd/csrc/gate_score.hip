@@ -359,7 +359,8 @@ __device__ __forceinline__ float silu_fast(float z) {
 // (256 rows) quarters it, with 2 or 4 times the matrix work per stage and
 // barrier; their A fragments are read in the stage that uses them rather
 // than one stage ahead, which would not fit the registers.  At RT = 4 a
-// stage's residual slot is 32 KiB, so three stages are in flight, not four.
+// stage's residual slot is 32 KiB and the accumulators take 128 registers,
+// so two stages are in flight (three slots), not four.
 template <int NTW, int NW, int NST, bool PACKED, int RT = 1>
 __global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
