@@ -127,6 +127,28 @@ def test_attn_bwd_masked_key_and_rows(D):
 
 
 @pytest.mark.parametrize("D", [128, 256])
+def test_attn_bwd_small_q_scale_deletes_keys(D):
+    """At per-query scales far below 1 (0.1 and 0.01) a -inf score still
+    deletes its key: rows that see only deleted keys get zero gradients,
+    deleted keys get zero dk, dv and dscore, and the rest matches the oracle
+    run on the keys that remain."""
+    rng = np.random.default_rng(94 + D)
+    N = 400
+    q, k, v, do, s, g, _ = make(rng, N, 8, 4, D)
+    c = np.where(np.arange(N) % 2 == 0, 0.1, 0.01).astype(np.float32)
+    s[:50] = -np.inf                      # rows 0..49 see only deleted keys
+    s[rng.choice(np.arange(50, N), 20, replace=False)] = -np.inf
+    dq, dk, dv, ds, dg = gpu_bwd(q, k, v, do, s, g, c)
+    dead = np.isneginf(s)
+    for t in (dk, dv):
+        assert torch.all(t[torch.from_numpy(dead)].float() == 0)
+    assert torch.all(dq[:50].float() == 0)
+    assert torch.all(ds.cpu()[torch.from_numpy(dead)] == 0)
+    ref = ref_bwd(q, k, v, do, s, g, c)
+    check((dq, dk, dv, ds, dg), ref, "attn_bwd_small_qscale_D%d" % D)
+
+
+@pytest.mark.parametrize("D", [128, 256])
 def test_attn_bwd_invariants_and_determinism(D):
     """sum_c dscore_c = 0 (a row's softmax ignores a shared shift of its
     scores) and two calls agree bit for bit."""
