@@ -362,12 +362,21 @@ attn_bf16_kernel(
         }
     }
 
-    float tmax = -INFINITY;
+    // tile max: one chain per 32-key half, each step taking two logits (one
+    // v_max3), then the two lane halves through a lane-half swap
+    float hmax[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      hmax[kb] = fmaxf(s[kb][0], s[kb][1]);
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) tmax = fmaxf(tmax, fmaxf(s[kb][r], s[kb][r + 1]));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      for (int r = 2; r < 16; r += 2) hmax[kb] = fmaxf(fmaxf(hmax[kb], s[kb][r]), s[kb][r + 1]);
+    }
+    float tmax = fmaxf(hmax[0], hmax[1]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
+                                                       false, false);
+      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
 
     // running max in log2 units (ac > 0 keeps the arg-max); maxima below
     // kMaskedLog2 are masked keys only
