@@ -361,24 +361,29 @@ __device__ __forceinline__ float silu_fast(float z) {
 // than one stage ahead, which would not fit the registers.  At RT = 4 a
 // stage's residual slot is 32 KiB and the accumulators take 128 registers,
 // so two stages are in flight (three slots), not four.
-template <int NTW, int NW, int NST, bool PACKED, int RT = 1>
-__global__ __launch_bounds__(NW * 64, 1) void gate_bf16_stream_kernel(
+// OCC = 2: two 64-row workgroups share each CU (at most 128 registers per
+// lane), each with two stages in flight and its A fragments read in the
+// stage that uses them; one workgroup's barrier and load waits then overlap
+// the other's matrix work.
+template <int NTW, int NW, int NST, bool PACKED, int RT = 1, int OCC = 1>
+__global__ __launch_bounds__(NW * 64, OCC) void gate_bf16_stream_kernel(
     const uint16_t* __restrict__ resid, int64_t ld_x, const uint8_t* __restrict__ prunable,
     float eps, const uint16_t* __restrict__ w1, const float* __restrict__ b1,
     const float* __restrict__ w2, float b2, float* __restrict__ scores, int32_t T, int32_t d,
     int32_t h, const int32_t* __restrict__ t_dyn) {
   constexpr int TM = 64 * RT;
   constexpr int MT = 4 * RT;                   // 16-row tiles
-  constexpr int DEPTH = RT == 4 ? 2 : kDepth;
+  constexpr int DEPTH = (RT == 4 || OCC == 2) ? 2 : kDepth;
   constexpr int R = DEPTH + 1;                 // ring length
   constexpr int XPW = 8 * RT / NW;             // residual blocks each wave loads per stage
   constexpr int PER_STAGE = XPW + 2 * NTW;     // vector-memory instructions per wave per stage
-  constexpr bool AHEAD = RT == 1;              // A fragments read one stage ahead
+  constexpr bool AHEAD = RT == 1 && OCC == 1;  // A fragments read one stage ahead
   // sum of squares: with 8 waves over 4 row tiles, wave w takes row tile
   // w & 3, k half w >> 2; otherwise wave w takes row tile w, both halves
   constexpr bool SS_HALVES = NW == 8 && RT == 1;
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(RT == 1 || ((RT == 2 || RT == 4) && NW == 8), "128/256-row tiles with 8 waves");
+  static_assert(OCC == 1 || (OCC == 2 && RT == 1 && NW == 8), "two workgroups per CU: 64 rows, 8 waves");
   static_assert(DEPTH >= 2 && R <= 8 && PER_STAGE * (DEPTH - 1) <= 63, "ring shape");
   using XS = XSlot<RT>;
   __shared__ __attribute__((aligned(16))) XS xs0, xs1, xs2, xs3, xs4, xs5, xs6, xs7;
@@ -764,7 +769,8 @@ void launch_bf16(bool has_gamma, int64_t T, dim3 grid, hipStream_t s, const uint
 // Streaming kernel dispatch: h = 16 * NTW * NW.  At h = 256 a prompt long
 // enough for two rounds of 256-row (or 128-row) workgroups on every CU takes
 // those tiles (a quarter or half of the W1 traffic per row); shorter ones
-// keep 64-row tiles, so that every CU still gets a workgroup.
+// keep 64-row tiles, so that every CU still gets a workgroup, two at a time
+// when there are at least two per CU (32k tokens: 5-8% faster than one).
 void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
                    const uint16_t* x, int64_t ld, const uint8_t* p, float eps,
                    const uint16_t* w, const float* b1, const float* w2, float b2, float* out,
@@ -773,27 +779,30 @@ void launch_stream(bool packed, int64_t T, int64_t h, int32_t d, hipStream_t s,
   const int64_t cus = device_cu_count();
   const bool rows256 = h == 256 && (T + 255) / 256 >= 2 * cus;
   const bool rows128 = h == 256 && (T + 127) / 128 >= 2 * cus;
-#define TG_GATE_STREAM(NTW, NW, NST, RT)                                                     \
+  const bool two64 = h == 256 && (T + 63) / 64 >= 2 * cus;
+#define TG_GATE_STREAM(NTW, NW, NST, RT, OCC)                                                \
   do {                                                                                      \
     const dim3 grid(static_cast<uint32_t>((T + 64 * RT - 1) / (64 * RT)));                  \
     if (packed)                                                                             \
-      gate_bf16_stream_kernel<NTW, NW, NST, true, RT><<<grid, dim3(NW * 64), 0, s>>>(       \
+      gate_bf16_stream_kernel<NTW, NW, NST, true, RT, OCC><<<grid, dim3(NW * 64), 0, s>>>(  \
           x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
     else                                                                                    \
-      gate_bf16_stream_kernel<NTW, NW, NST, false, RT><<<grid, dim3(NW * 64), 0, s>>>(      \
+      gate_bf16_stream_kernel<NTW, NW, NST, false, RT, OCC><<<grid, dim3(NW * 64), 0, s>>>( \
           x, ld, p, eps, w, b1, w2, b2, out, T32, d, h32, t_dyn);                           \
   } while (0)
   if (h == 256 && d == 2048) {   // Qwen3-1.7B hidden size, h = 256
-    if (rows256) TG_GATE_STREAM(2, 8, 32, 4);
-    else if (rows128) TG_GATE_STREAM(2, 8, 32, 2);
-    else TG_GATE_STREAM(2, 8, 32, 1);
+    if (rows256) TG_GATE_STREAM(2, 8, 32, 4, 1);
+    else if (rows128) TG_GATE_STREAM(2, 8, 32, 2, 1);
+    else if (two64) TG_GATE_STREAM(2, 8, 32, 1, 2);
+    else TG_GATE_STREAM(2, 8, 32, 1, 1);
   } else if (h == 256) {
-    if (rows256) TG_GATE_STREAM(2, 8, 0, 4);
-    else if (rows128) TG_GATE_STREAM(2, 8, 0, 2);
-    else TG_GATE_STREAM(2, 8, 0, 1);
-  } else if (h == 192) TG_GATE_STREAM(3, 4, 0, 1);
-  else if (h == 128) TG_GATE_STREAM(2, 4, 0, 1);
-  else TG_GATE_STREAM(1, 4, 0, 1);
+    if (rows256) TG_GATE_STREAM(2, 8, 0, 4, 1);
+    else if (rows128) TG_GATE_STREAM(2, 8, 0, 2, 1);
+    else if (two64) TG_GATE_STREAM(2, 8, 0, 1, 2);
+    else TG_GATE_STREAM(2, 8, 0, 1, 1);
+  } else if (h == 192) TG_GATE_STREAM(3, 4, 0, 1, 1);
+  else if (h == 128) TG_GATE_STREAM(2, 4, 0, 1, 1);
+  else TG_GATE_STREAM(1, 4, 0, 1, 1);
 #undef TG_GATE_STREAM
 }
 

@@ -131,6 +131,33 @@ def test_gate_bf16_stream_128_rows(T, d, with_b1, frac, packed):
 
 
 @pytest.mark.parametrize("T,d,with_b1,frac", [
+    (33001, 2048, True, 0.8),   # two 64-row workgroups per CU, 32-stage kernel, ragged tail
+    (40000, 1088, False, 0.6),  # the same, 17 stages (the ring wraps partway)
+])
+@pytest.mark.parametrize("packed", [False, True])
+def test_gate_bf16_stream_two_per_cu(T, d, with_b1, frac, packed):
+    """At h = 256, prompts with two rounds of 64-row workgroups per CU but
+    not two of 128-row ones (32768 < T < 65409 on 256 CUs) run two
+    workgroups on each CU at a time: against the oracle on the first and
+    last rows, every workgroup's first and last rows, and random rows."""
+    args = _random_case(T, d, 256, False, with_b1, frac)
+    resid, prunable, w1, w2, b2, gamma, b1, eps, dt = args
+    got = run_gpu(*args, stride_pad=8 if T % 2 else 0, packed=packed)
+    rng = np.random.default_rng(T + d)
+    edges = np.arange(0, T, 64)
+    rows = np.unique(np.concatenate([
+        np.arange(0, 200), np.arange(T - 200, T), edges, np.minimum(edges + 63, T - 1),
+        rng.choice(T, size=2000, replace=False)]))
+    sub = np.zeros(T, np.uint8)
+    sub[rows] = prunable[rows]
+    ref = run_oracle(resid[rows], sub[rows], w1, w2, b2, gamma, b1, eps, dt)
+    assert np.all(got[prunable == 0] == 0)
+    assert np.count_nonzero(got) <= int(prunable.sum())
+    assert_close_abs(got[rows], ref, BF16_ABS,
+                     "gate_bf16_stream2wg_T%d_d%d_%s" % (T, d, "packed" if packed else "rowmajor"))
+
+
+@pytest.mark.parametrize("T,d,with_b1,frac", [
     (131172, 2048, True, 0.8),   # 256-row tiles, 32-stage kernel, ragged last tile
     (140001, 1088, False, 0.6),  # 256-row tiles, 17 stages (the ring wraps partway)
 ])
