@@ -7,8 +7,12 @@
 // budget None keeps every prunable token.
 //
 // Design (gfx950).  Scores become order-preserving u32 keys (NaN lowest,
-// -0 == +0).  Three histogram passes over digits of 11, 11 and 10 bits find
-// the K-th largest key v*: every workgroup builds an LDS histogram of the
+// -0 == +0).  Three paths by prompt length: T <= 24576, one workgroup with
+// every key in LDS; T <= 524288 (the grid path below), one launch of up to
+// 32 workgroups that meet at grid barriers; longer prompts, the four
+// launches described here.  Three histogram passes over digits of 11, 11
+// and 10 bits find the K-th largest key v*: every workgroup builds an LDS
+// histogram of the
 // keys that still match the resolved prefix and adds it to a global one;
 // the last workgroup to arrive (device-scope counter, no grid barrier)
 // picks the digit whose bucket holds the K-th key and updates the prefix.
@@ -22,9 +26,11 @@
 // a workgroup only ever waits on workgroups that are already running.
 //
 // Workspace: global histograms, pass counters, the resolved state and the
-// look-back descriptors.  It must start all-zero; the last workgroup of each
-// pass clears what that pass used, so every call ends with it all-zero.  The
-// first histogram pass also resets the compaction's ticket and descriptors.
+// look-back descriptors (or, on the grid path, its barrier counters and
+// per-workgroup counts in the descriptors' place).  It must start all-zero;
+// the last workgroup of each pass (of the grid launch) clears what it used,
+// so every call ends with it all-zero.  The first histogram pass also resets
+// the compaction's ticket and descriptors.
 #include <mutex>
 
 #include "tg_common.hpp"
@@ -722,6 +728,335 @@ __global__ __launch_bounds__(kOneThreads) void select_one_wg_kernel(
   if (tid == 0) n_kept[0] = static_cast<int32_t>(tot_a + (tot_b < need ? tot_b : need));
 }
 
+// ---------------------------------------------------------------------------
+// Grid path (kGridMinT < T <= kGridMaxT): the whole selection in one launch
+// of G <= kGridMaxWG workgroups that are resident together (at most one per
+// CU, far fewer than the CUs).  Each stages its range of `per` tokens in LDS
+// once, as the single-workgroup kernel does; the digit passes then add the
+// workgroups' LDS histograms into global ones and meet at a grid barrier,
+// after which every workgroup reads the global histogram and resolves the
+// digit itself (the same result everywhere, so every workgroup takes the
+// same branches and barriers).  The compaction publishes each workgroup's
+// (a, b) counts, meets at a last barrier and adds its predecessors' counts.
+// A barrier is a counter per barrier: each workgroup adds 1 after its
+// writes, then waits for G.  The wait is bounded (kSpinLimit polls); one that
+// gives up marks the call failed, which its last workgroup reports as
+// n_kept = -1, so a workgroup that never ran could not hang the device.
+// The last workgroup to finish clears every counter and histogram.
+// ---------------------------------------------------------------------------
+constexpr int kGridThreads = 1024;
+constexpr int kGridMaxWG = 32;
+constexpr int kGridPer = 4096;                                    // tokens per workgroup, up to ...
+constexpr int kGridPerMax = 16384;                                // ... this (64 KiB of keys)
+constexpr int64_t kGridMinT = 24576;   // below it the single workgroup is faster (20k: 14.9 vs 16.9 us)
+constexpr int64_t kGridMaxT = static_cast<int64_t>(kGridMaxWG) * kGridPerMax;
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+// Grid path control, at kFlagOff (the compaction descriptors' space, which
+// the grid path does not use): all-zero between calls.
+struct GridCtl {
+  uint32_t arrive[5];    // barrier counters: digit passes 0..2, |P|, compaction
+  uint32_t exit_count;   // workgroups done
+  uint32_t n_p;          // sum of the workgroups' prunable counts
+  uint32_t timeout;      // some barrier wait gave up
+  uint64_t slot[kGridMaxWG];   // workgroup g's (a count << 32) | b count
+};
+
+// Everything one workgroup hands to another goes through device-coherent
+// operations: atomics (performed at the device's coherence point, as the
+// cross-workgroup sums here rely on) and agent-scope loads and stores, which
+// bypass the non-coherent caches.  So a barrier needs no cache write-back:
+// every wave waits until its own memory operations have completed (a
+// workgroup-scope release), then thread 0 arrives and waits for all G.
+__device__ __forceinline__ void grid_barrier(uint32_t* count, uint32_t G, uint32_t* timeout) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt and lgkmcnt all 0
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t polls = 0;
+    while (ld_agent(count) < G) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls > kSpinLimit) {
+        atomicOr(timeout, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int MAXT>
+__global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
+    const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
+    int32_t per, uint32_t K, int32_t* __restrict__ kept_idx, int64_t capacity,
+    int32_t* __restrict__ n_kept, uint8_t* __restrict__ ws, const int32_t* __restrict__ t_dyn) {
+  constexpr int NCOPY = MAXT <= kGridPer ? 8 : 2;
+  constexpr int NW = kGridThreads / 64;
+  if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
+  __shared__ __attribute__((aligned(16))) uint32_t keys[MAXT];
+  __shared__ uint32_t hist[2048];
+  __shared__ __attribute__((aligned(16))) uint32_t histc[2048 * NCOPY];
+  __shared__ uint32_t s_wave[2 * NW];
+  __shared__ uint32_t s_state[4];   // prefix, mask, need, resolved
+  __shared__ uint32_t s_np[NW];
+  __shared__ uint32_t s_pre[2];
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const uint32_t G = gridDim.x;
+  const uint32_t g = blockIdx.x;
+  GridCtl* ctl = reinterpret_cast<GridCtl*>(ws + kFlagOff);
+
+  // this workgroup's tokens [begin, begin + nloc); per is a multiple of 16,
+  // so the 16-byte loads below stay aligned
+  const int64_t begin = static_cast<int64_t>(g) * per;
+  const int32_t nloc = static_cast<int32_t>(
+      begin >= T ? 0 : (T - begin < per ? T - begin : static_cast<int64_t>(per)));
+  const __amdgpu_buffer_rsrc_t p_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(prunable + begin), 0, nloc, 0x00020000);
+  const __amdgpu_buffer_rsrc_t s_rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scores + begin), 0, nloc * 4, 0x00020000);
+  uint32_t np = 0;
+  for (int base = 0; base < nloc; base += kGridThreads * 16) {
+    const int t0 = base + tid * 16;
+    if (t0 < nloc) {
+      u32x4 pm = __builtin_amdgcn_raw_buffer_load_b128(p_rs, t0, 0, 0);
+      u32x4 sv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sv[j] = __builtin_amdgcn_raw_buffer_load_b128(s_rs, (t0 + 4 * j) * 4, 0, 0);
+      if (t0 + 16 > nloc) {   // the range check is per dword: fetch the tail bytewise
+        pm = u32x4{0, 0, 0, 0};
+        for (int e = 0; t0 + e < nloc; ++e)
+          pm[e >> 2] |= static_cast<uint32_t>(prunable[begin + t0 + e] != 0) << (8 * (e & 3));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 kv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool p = ((pm[j] >> (8 * e)) & 0xffu) != 0;
+          kv[e] = p ? score_key(__uint_as_float(sv[j][e])) + 1u : 0u;
+          np += p;
+        }
+        *reinterpret_cast<u32x4*>(&keys[t0 + 4 * j]) = kv;   // t0 + 15 < per <= MAXT
+      }
+    }
+  }
+
+  // |P| over all workgroups, when K could reach it (K >= T / 2, or K == 0)
+  const bool count_p = K == 0 || 2 * static_cast<int64_t>(K) >= T;
+  uint32_t n_p = 0xffffffffu;   // |P|, or "unknown"
+  if (count_p) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) np += __shfl_xor(np, off, 64);
+    if (lane == 0) s_np[tid >> 6] = np;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c += s_np[w];
+      if (c) atomicAdd(&ctl->n_p, c);
+    }
+    grid_barrier(&ctl->arrive[3], G, &ctl->timeout);
+    n_p = ld_agent(&ctl->n_p);
+  }
+
+  const bool all_or_none = count_p && (K >= n_p || K == 0);
+  uint32_t prefix = 0, mask = 0, need = all_or_none ? (K >= n_p ? n_p : 0u) : K;
+  if (!all_or_none) {
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int bits = pass == 2 ? 10 : 11;
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t nb = 1u << bits;
+      uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + kHistOff[pass]);
+      for (int b = tid; b < 2048; b += kGridThreads) hist[b] = 0;
+      if (pass == 0)
+#pragma unroll
+        for (int b = 4 * tid; b < 2048 * NCOPY; b += 4 * kGridThreads)
+          *reinterpret_cast<u32x4*>(&histc[b]) = u32x4{0, 0, 0, 0};
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < MAXT / (4 * kGridThreads); ++i) {
+        const int t = 4 * tid + 4 * kGridThreads * i;
+        if (t < nloc) {
+          const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t k = kv[e];
+            if (k != 0 && (k & mask) == prefix) {
+              const uint32_t bin = (k >> shift) & (nb - 1);
+              if (pass == 0)
+                atomicAdd(&histc[bin * NCOPY + (lane & (NCOPY - 1))], 1u);
+              else
+                atomicAdd(&hist[bin], 1u);
+            }
+          }
+        }
+      }
+      __syncthreads();
+      // fold the first digit's copies, and add the nonzero bins to the
+      // global histogram
+      for (uint32_t b = tid; b < nb; b += kGridThreads) {
+        uint32_t c;
+        if (pass == 0) {
+          c = 0;
+#pragma unroll
+          for (int j = 0; j < NCOPY; j += 2) {
+            const u32x2 v2 = *reinterpret_cast<const u32x2*>(&histc[b * NCOPY + j]);
+            c += v2[0] + v2[1];
+          }
+        } else {
+          c = hist[b];
+        }
+        if (c) atomicAdd(&ghist[b], c);
+      }
+      grid_barrier(&ctl->arrive[pass], G, &ctl->timeout);
+      for (uint32_t b = tid; b < nb; b += kGridThreads) hist[b] = ld_agent(&ghist[b]);
+      __syncthreads();
+      if (tid < 64) {
+        // the single-workgroup kernel's resolve: lane l owns bins
+        // nb-1-l*bpl down to nb-(l+1)*bpl (descending keys)
+        const int bpl = static_cast<int>(nb) / 64;
+        const int top = static_cast<int>(nb) - 1 - lane * bpl;
+        uint32_t cnt[32];
+        uint32_t mine = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          cnt[j] = j < bpl ? hist[top - j] : 0u;
+          mine += cnt[j];
+        }
+        const uint32_t incl = wave_inclusive_scan(mine);
+        const uint32_t total = __shfl(incl, 63, 64);
+        uint32_t nd = need;
+        if (lane == 0) s_state[3] = 0;
+        if (pass == 0) {   // total = |P|: every prunable key matches the empty prefix
+          if (K >= total || K == 0) {
+            if (lane == 0) {
+              s_state[0] = 0;
+              s_state[1] = 0;
+              s_state[2] = K >= total ? total : 0u;
+              s_state[3] = 1;
+            }
+            nd = 0;
+          }
+        }
+        const uint32_t above = incl - mine;
+        if (nd != 0 && above < nd && nd <= above + mine) {
+          uint32_t cum = above;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) {
+            const uint32_t c = cnt[j];
+            if (cum < nd && cum + c >= nd) {
+              s_state[0] = prefix | (static_cast<uint32_t>(top - j) << shift);
+              s_state[1] = mask | ((nb - 1) << shift);
+              s_state[2] = nd - cum;
+              s_state[3] = (nd - cum == c || pass == 2) ? 1u : 0u;
+            }
+            cum += c;
+          }
+        }
+      }
+      __syncthreads();
+      prefix = s_state[0];
+      mask = s_state[1];
+      need = s_state[2];
+      const bool resolved = s_state[3] != 0;
+      __syncthreads();   // every thread has read the state before the next pass
+      if (resolved) break;   // the same in every workgroup
+    }
+  }
+
+  // ordered compaction: thread tid owns the contiguous tokens
+  // [tid * C, tid * C + C) of the range, C a multiple of 4
+  const int C = ((nloc + kGridThreads - 1) / kGridThreads + 3) & ~3;
+  const int c0 = tid * C;
+  uint32_t ca = 0, cb = 0;
+  for (int i = 0; i < C; i += 4) {
+    if (c0 + i < nloc) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[c0 + i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t k = kv[e];
+        const bool in = c0 + i + e < nloc;
+        const uint32_t km = k & mask;
+        ca += in && (k == 0 || km > prefix);
+        cb += in && k != 0 && km == prefix;
+      }
+    }
+  }
+  uint32_t xa = ca, xb = cb, tot_a = 0, tot_b = 0;
+  wg_inclusive_scan2(xa, xb, s_wave, tot_a, tot_b);
+  if (tid == 0) st_agent(&ctl->slot[g], (static_cast<uint64_t>(tot_a) << 32) | tot_b);
+  grid_barrier(&ctl->arrive[4], G, &ctl->timeout);
+  if (tid < 64) {   // the counts of the workgroups before this one (G <= 64)
+    const uint64_t v = lane < static_cast<int>(g) ? ld_agent(&ctl->slot[lane]) : 0ull;
+    uint32_t pa = static_cast<uint32_t>(v >> 32), pb = static_cast<uint32_t>(v);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      pa += __shfl_xor(pa, off, 64);
+      pb += __shfl_xor(pb, off, 64);
+    }
+    if (lane == 0) {
+      s_pre[0] = pa;
+      s_pre[1] = pb;
+    }
+  }
+  __syncthreads();
+  xa = xa - ca + s_pre[0];   // exclusive prefixes over the whole prompt
+  xb = xb - cb + s_pre[1];
+  for (int i = 0; i < C; i += 4) {
+    if (c0 + i < nloc) {
+      const u32x4 kv = *reinterpret_cast<const u32x4*>(&keys[c0 + i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = c0 + i + e;
+        const uint32_t k = kv[e];
+        const uint32_t km = k & mask;
+        const bool fa = t < nloc && (k == 0 || km > prefix);
+        const bool fb = t < nloc && k != 0 && km == prefix;
+        if (fa || (fb && xb < need)) {
+          const int64_t slot = static_cast<int64_t>(xa) + (xb < need ? xb : need);
+          if (slot < capacity) kept_idx[slot] = static_cast<int32_t>(begin + t);
+        }
+        xa += fa;
+        xb += fb;
+      }
+    }
+  }
+
+  // the last workgroup to finish writes the kept count and clears the
+  // control words and histograms (every workgroup has passed every barrier
+  // and read every histogram by then)
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&ctl->exit_count, 1u) == G - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (tid == 0) {
+    // the totals over every workgroup's slot (the last to finish may be any)
+    uint64_t all_a = 0, all_b = 0;
+    for (uint32_t j = 0; j < G; ++j) {
+      const uint64_t v = ld_agent(&ctl->slot[j]);
+      all_a += v >> 32;
+      all_b += static_cast<uint32_t>(v);
+    }
+    const bool failed = ld_agent(&ctl->timeout) != 0;
+    n_kept[0] = failed ? -1
+                       : static_cast<int32_t>(all_a + (all_b < need ? all_b : static_cast<uint64_t>(need)));
+    for (int j = 0; j < 5; ++j) st_agent(&ctl->arrive[j], 0u);
+    st_agent(&ctl->n_p, 0u);
+    st_agent(&ctl->timeout, 0u);
+    st_agent(&ctl->exit_count, 0u);
+  }
+  for (int j = tid; j < kGridMaxWG; j += kGridThreads) st_agent(&ctl->slot[j], static_cast<uint64_t>(0));
+  for (int b = tid; b < 2048 + 2048 + 1024; b += kGridThreads)
+    st_agent(reinterpret_cast<uint32_t*>(ws + kHistOff[0]) + b, 0u);
+}
+
 }  // namespace
 }  // namespace tg
 
@@ -729,7 +1064,8 @@ extern "C" size_t tg_topk_workspace_size(int64_t T) {
   using namespace tg;
   if (T < 0) T = 0;
   const int64_t G = blocks_for(T, nullptr);
-  const size_t bytes = kFlagOff + static_cast<size_t>(G) * sizeof(uint64_t);
+  size_t bytes = kFlagOff + static_cast<size_t>(G) * sizeof(uint64_t);
+  if (bytes < kFlagOff + sizeof(GridCtl)) bytes = kFlagOff + sizeof(GridCtl);   // grid path
   return (bytes + 255) & ~static_cast<size_t>(255);
 }
 
@@ -802,6 +1138,22 @@ tg_status select_launch(const char* fn, int64_t T, const float* scores,
     return check_launch(fn);
   }
   const uint32_t Kc = static_cast<uint32_t>(K < T ? K : T);
+  if (T > kGridMinT && T <= kGridMaxT && aligned(prunable, 16)) {
+    // one launch, G workgroups resident together (G <= kGridMaxWG, far
+    // below the CU count; each takes at most one CU)
+    const int64_t G = std::min<int64_t>(kGridMaxWG, (T + kGridPer - 1) / kGridPer);
+    const int64_t per = ((T + G - 1) / G + 15) / 16 * 16;
+    const int32_t T32 = static_cast<int32_t>(T);
+    if (per <= kGridPer)
+      select_grid_kernel<kGridPer><<<dim3(G), dim3(kGridThreads), 0, s>>>(
+          scores, prunable, T32, static_cast<int32_t>(per), Kc, kept_idx, kept_capacity, n_kept,
+          ws, t_dyn);
+    else
+      select_grid_kernel<kGridPerMax><<<dim3(G), dim3(kGridThreads), 0, s>>>(
+          scores, prunable, T32, static_cast<int32_t>(per), Kc, kept_idx, kept_capacity, n_kept,
+          ws, t_dyn);
+    return check_launch(fn);
+  }
   if (T <= kLdsTokens && aligned(prunable, 16)) {
     if (T <= kLdsTokens / 2)
       select_one_wg_kernel<kLdsTokens / 2><<<dim3(1), dim3(kOneThreads), 0, s>>>(

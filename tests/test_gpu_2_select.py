@@ -47,7 +47,8 @@ def _scores(rng, T, kind):
     return s
 
 
-@pytest.mark.parametrize("T", [1, 7, 1000, 1023, 1024, 1025, 4097, 16384, 32767, 32768, 32769, 100003])
+@pytest.mark.parametrize("T", [1, 7, 1000, 1023, 1024, 1025, 4097, 16384, 24576, 24577, 32767,
+                               32768, 32769, 100003, 524288, 524289])
 @pytest.mark.parametrize("kind", ["normal", "ties", "special", "equal", "few"])
 def test_select_random(T, kind):
     rng = np.random.default_rng(T + len(kind))
