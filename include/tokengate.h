@@ -161,7 +161,12 @@ tg_status tg_gate_score_packed(tg_dtype dt, int64_t T, int64_t d, int64_t h,
  *                kept_capacity are dropped (so a capacity of T is always
  *                enough).
  * n_kept         out, [1] int32 on the device: the kept count N (may exceed
- *                kept_capacity, which signals a too-small capacity).
+ *                kept_capacity, which signals a too-small capacity).  For
+ *                24576 < T <= 524288 the selection is one launch of at most
+ *                32 workgroups that wait for each other (at most one per
+ *                CU); a wait is bounded, and if one gives up (the workgroups
+ *                were not all running together) n_kept is -1 and kept_idx
+ *                is invalid.
  * workspace      device scratch of at least tg_topk_workspace_size(T) bytes,
  *                256-byte aligned.  It must be all-zero before its first use;
  *                every call leaves it all-zero again when its kernels finish.

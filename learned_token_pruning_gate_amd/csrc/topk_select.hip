@@ -31,6 +31,7 @@
 // the last workgroup of each pass (of the grid launch) clears what it used,
 // so every call ends with it all-zero.  The first histogram pass also resets
 // the compaction's ticket and descriptors.
+#include <cstdlib>
 #include <mutex>
 
 #include "tg_common.hpp"
@@ -768,16 +769,19 @@ struct GridCtl {
 // bypass the non-coherent caches.  So a barrier needs no cache write-back:
 // every wave waits until its own memory operations have completed (a
 // workgroup-scope release), then thread 0 arrives and waits for all G.
-__device__ __forceinline__ void grid_barrier(uint32_t* count, uint32_t G, uint32_t* timeout) {
+// `want` is G in every call but the forced-timeout check (below), and
+// `limit` the poll bound.
+__device__ __forceinline__ void grid_barrier(uint32_t* count, uint32_t want, uint32_t limit,
+                                             uint32_t* timeout) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);   // vmcnt, expcnt and lgkmcnt all 0
   __syncthreads();
   if (threadIdx.x == 0) {
     __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t polls = 0;
-    while (ld_agent(count) < G) {
+    while (ld_agent(count) < want) {
       __builtin_amdgcn_s_sleep(1);
-      if (++polls > kSpinLimit) {
+      if (++polls > limit) {
         atomicOr(timeout, 1u);
         break;
       }
@@ -790,7 +794,8 @@ template <int MAXT>
 __global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
     const float* __restrict__ scores, const uint8_t* __restrict__ prunable, int32_t T,
     int32_t per, uint32_t K, int32_t* __restrict__ kept_idx, int64_t capacity,
-    int32_t* __restrict__ n_kept, uint8_t* __restrict__ ws, const int32_t* __restrict__ t_dyn) {
+    int32_t* __restrict__ n_kept, uint8_t* __restrict__ ws, const int32_t* __restrict__ t_dyn,
+    uint32_t extra, uint32_t limit) {
   constexpr int NCOPY = MAXT <= kGridPer ? 8 : 2;
   constexpr int NW = kGridThreads / 64;
   if (t_dyn != nullptr) T = min(T, max(*t_dyn, 0));   // run-time length (T: capacity)
@@ -805,6 +810,7 @@ __global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const uint32_t G = gridDim.x;
+  const uint32_t want = G + extra;   // arrivals a barrier waits for
   const uint32_t g = blockIdx.x;
   GridCtl* ctl = reinterpret_cast<GridCtl*>(ws + kFlagOff);
 
@@ -859,7 +865,7 @@ __global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
       for (int w = 0; w < NW; ++w) c += s_np[w];
       if (c) atomicAdd(&ctl->n_p, c);
     }
-    grid_barrier(&ctl->arrive[3], G, &ctl->timeout);
+    grid_barrier(&ctl->arrive[3], want, limit, &ctl->timeout);
     n_p = ld_agent(&ctl->n_p);
   }
 
@@ -913,7 +919,7 @@ __global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
         }
         if (c) atomicAdd(&ghist[b], c);
       }
-      grid_barrier(&ctl->arrive[pass], G, &ctl->timeout);
+      grid_barrier(&ctl->arrive[pass], want, limit, &ctl->timeout);
       for (uint32_t b = tid; b < nb; b += kGridThreads) hist[b] = ld_agent(&ghist[b]);
       __syncthreads();
       if (tid < 64) {
@@ -990,7 +996,7 @@ __global__ __launch_bounds__(kGridThreads) void select_grid_kernel(
   uint32_t xa = ca, xb = cb, tot_a = 0, tot_b = 0;
   wg_inclusive_scan2(xa, xb, s_wave, tot_a, tot_b);
   if (tid == 0) st_agent(&ctl->slot[g], (static_cast<uint64_t>(tot_a) << 32) | tot_b);
-  grid_barrier(&ctl->arrive[4], G, &ctl->timeout);
+  grid_barrier(&ctl->arrive[4], want, limit, &ctl->timeout);
   if (tid < 64) {   // the counts of the workgroups before this one (G <= 64)
     const uint64_t v = lane < static_cast<int>(g) ? ld_agent(&ctl->slot[lane]) : 0ull;
     uint32_t pa = static_cast<uint32_t>(v >> 32), pb = static_cast<uint32_t>(v);
@@ -1144,14 +1150,24 @@ tg_status select_launch(const char* fn, int64_t T, const float* scores,
     const int64_t G = std::min<int64_t>(kGridMaxWG, (T + kGridPer - 1) / kGridPer);
     const int64_t per = ((T + G - 1) / G + 15) / 16 * 16;
     const int32_t T32 = static_cast<int32_t>(T);
+    // TG_TEST_SELECT_TIMEOUT=1 (read once) makes every barrier wait for one
+    // arrival more than there are workgroups, with a short poll bound: the
+    // waits give up and the call reports n_kept = -1.  The failure path is
+    // tested this way, with every workgroup still exiting normally.
+    static const bool force_timeout = [] {
+      const char* e = std::getenv("TG_TEST_SELECT_TIMEOUT");
+      return e != nullptr && e[0] == '1';
+    }();
+    const uint32_t extra = force_timeout ? 1u : 0u;
+    const uint32_t limit = force_timeout ? 256u : kSpinLimit;
     if (per <= kGridPer)
       select_grid_kernel<kGridPer><<<dim3(G), dim3(kGridThreads), 0, s>>>(
           scores, prunable, T32, static_cast<int32_t>(per), Kc, kept_idx, kept_capacity, n_kept,
-          ws, t_dyn);
+          ws, t_dyn, extra, limit);
     else
       select_grid_kernel<kGridPerMax><<<dim3(G), dim3(kGridThreads), 0, s>>>(
           scores, prunable, T32, static_cast<int32_t>(per), Kc, kept_idx, kept_capacity, n_kept,
-          ws, t_dyn);
+          ws, t_dyn, extra, limit);
     return check_launch(fn);
   }
   if (T <= kLdsTokens && aligned(prunable, 16)) {

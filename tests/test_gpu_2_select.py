@@ -129,3 +129,41 @@ def test_select_determinism():
     a, na = gpu_select(s, p, 2000)
     b, nb = gpu_select(s, p, 2000)
     assert na == nb and np.array_equal(a[:na], b[:nb])
+
+
+_TIMEOUT_CHILD = r"""
+import torch
+import learned_token_pruning_gate_amd as tg
+dev = torch.device("cuda", 0)
+g = torch.Generator(device=dev).manual_seed(3)
+for T, K, grid in ((40000, 1000, True), (1000, 100, False)):
+    s = torch.randn(T, generator=g, device=dev)
+    p = torch.ones(T, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(tg.tg_topk_workspace_size(T), dtype=torch.uint8, device=dev)
+    kept = torch.full((T,), -5, dtype=torch.int32, device=dev)
+    kept, n = tg.tg_topk_select(s, p, K, kept_idx=kept, workspace=ws)
+    torch.cuda.synchronize()
+    want = -1 if grid else K
+    assert int(n.item()) == want, (T, int(n.item()), want)
+    assert int(ws.count_nonzero().item()) == 0, "workspace not left zeroed"
+print("timeout path ok")
+"""
+
+
+def test_select_grid_timeout_reported():
+    """The grid path's barrier waits are bounded.  Forced to give up (with
+    TG_TEST_SELECT_TIMEOUT=1 every barrier waits for one arrival more than
+    there are workgroups, with a short poll bound), the call still ends,
+    reports n_kept = -1 and leaves the workspace zeroed; a short prompt (one
+    workgroup, no barrier) in the same process is unaffected.  Runs in a
+    child process, since the library reads the variable once."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, TG_TEST_SELECT_TIMEOUT="1",
+               PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", _TIMEOUT_CHILD], env=env, cwd=root,
+                       capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "timeout path ok" in r.stdout
