@@ -101,6 +101,9 @@ __device__ __forceinline__ float bf16_val(uint32_t bits) {
 // kMaskedLog2 counts as "no visible key" (a -inf score is encoded as a bias
 // far below it).
 constexpr float kMaskedLog2 = -524288.0f;
+// How far (log2 units) a tile's max may exceed the running reference before
+// the output is rescaled to it.
+constexpr float kLazyMax = 8.0f;
 
 // The bias of a key tile is the initial value of the logit accumulators: in
 // the 32x32 accumulator layout, lane (query, half hh) holds in register r of
@@ -382,18 +385,21 @@ attn_bf16_kernel(
     // kMaskedLog2 are masked keys only
     float tm = tmax * ac;
     tm = tm > kMaskedLog2 ? tm : -INFINITY;
-    const float m_new = fmaxf(m_run, tm);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    if (__any(m_new > m_run)) {
-      // 0 when nothing was accumulated yet
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_use);
+    // the reference max moves only when some lane's tile max exceeds its
+    // reference by more than kLazyMax (then every lane moves to its own
+    // running max); in between, weights 2^(y - m) reach at most 2^kLazyMax
+    if (__any(tm > m_run + kLazyMax)) {
+      const float m_new = fmaxf(m_run, tm);
+      // 0 when nothing was accumulated yet; 1 for a lane whose max held
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       l_run *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
 
     // P^T = 2^(y - m) as bf16, already laid out as the PV B operand; the row
     // maximum gets weight exactly 1
