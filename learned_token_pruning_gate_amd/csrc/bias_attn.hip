@@ -50,7 +50,8 @@
 //     initial value of the logit accumulators, so the MFMAs add the dot
 //     products to it; logits use exp2 with log2(e) folded into the scale;
 //     the output is rescaled only when some query's tile max exceeds its
-//     reference max by more than 2^8 (weights stay below 2^8 in between).
+//     reference max by more than 8 in log2 units (weights stay at most 2^8
+//     in between).
 //   * Workgroups are ordered longest-first (causal) and the KV head is the
 //     fastest-varying index, so consecutive workgroups -- which the
 //     dispatcher spreads over the 8 XCDs -- keep one KV head per XCD L2.
