@@ -48,10 +48,12 @@
 //   * The bias gain_h*score_c (in dot-product units) is formed once per key
 //     tile and head in LDS, in the accumulator layout's key order, and is the
 //     initial value of the logit accumulators, so the MFMAs add the dot
-//     products to it; logits use exp2 with log2(e) folded into the scale;
-//     the output is rescaled only when some query's tile max exceeds its
-//     reference max by more than 8 in log2 units (weights stay at most 2^8
-//     in between).
+//     products to it; logits use exp2 with log2(e) folded into the scale.
+//   * The weights' reference is not the running max: a tile's max is taken,
+//     and the output rescaled to it, only until every query has one, or
+//     when a tile's weights would take some query's running sum past 2^32.
+//     The running sum adds the bf16 weights that the PV product uses (two
+//     per v_dot2c_f32_bf16), so the normaliser and P^T agree key by key.
 //   * Workgroups are ordered longest-first (causal) and the KV head is the
 //     fastest-varying index, so consecutive workgroups -- which the
 //     dispatcher spreads over the 8 XCDs -- keep one KV head per XCD L2.
@@ -103,9 +105,9 @@ __device__ __forceinline__ float bf16_val(uint32_t bits) {
 // kMaskedLog2 counts as "no visible key" (a -inf score is encoded as a bias
 // far below it).
 constexpr float kMaskedLog2 = -524288.0f;
-// How far (log2 units) a tile's max may exceed the running reference before
-// the output is rescaled to it.
-constexpr float kLazyMax = 8.0f;
+// The running sum of weights 2^(y - m) that makes the reference m move to the
+// running max (and the output rescale to it).
+constexpr float kSumCap = 0x1p32f;
 
 // The bias of a key tile is the initial value of the logit accumulators: in
 // the 32x32 accumulator layout, lane (query, half hh) holds in register r of
@@ -282,7 +284,10 @@ attn_bf16_kernel(
       qf[ks] = __builtin_bit_cast(bf16x8,
                                   __builtin_amdgcn_raw_buffer_load_b128(q_rs, base + 32u * ks, 0, 0));
   }
-  float m_run = -INFINITY;  // running max of y over visible keys (log2 units)
+  // reference of the weights 2^(y - m) (log2 units): -inf until a visible
+  // key, then some running max of y that the weights never exceed by 32
+  float m_run = -INFINITY;
+  float m_use = 0.0f;       // m_run, or 0 while it is -inf
   const int lim = CAUSAL ? min(my_q, Ne - 1) : Ne - 1;   // last visible key
 
   // ---- running state --------------------------------------------------------
@@ -367,30 +372,60 @@ attn_bf16_kernel(
         }
     }
 
-    // tile max: one chain per 32-key half, each step taking two logits (one
-    // v_max3), then the two lane halves through a lane-half swap
-    float hmax[2];
+    // P^T = 2^(y - m) as bf16, already laid out as the PV B operand, with
+    // the lane's reference m; lt is the running sum with this tile added.
+    // The sum adds the bf16 weights themselves (two per v_dot2c with a pair
+    // of ones), so the normaliser weighs each key exactly as P^T does.
+    bf16x8 p[2][2];
+    float lt;
+    auto weights = [&]() __attribute__((always_inline)) {
+      lt = l_run;
+      const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      hmax[kb] = fmaxf(s[kb][0], s[kb][1]);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 2; r < 16; r += 2) hmax[kb] = fmaxf(fmaxf(hmax[kb], s[kb][r]), s[kb][r + 1]);
-    }
-    float tmax = fmaxf(hmax[0], hmax[1]);
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax), __float_as_uint(tmax),
-                                                       false, false);
-      tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-
-    // running max in log2 units (ac > 0 keeps the arg-max); maxima below
-    // kMaskedLog2 are masked keys only
-    float tm = tmax * ac;
-    tm = tm > kMaskedLog2 ? tm : -INFINITY;
-    // the reference max moves only when some lane's tile max exceeds its
-    // reference by more than kLazyMax (then every lane moves to its own
-    // running max); in between, weights 2^(y - m) reach at most 2^kLazyMax
-    if (__any(tm > m_run + kLazyMax)) {
+        for (int hf = 0; hf < 2; ++hf) {
+          bf16x2 pr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + 2 * i], ac, -m_use));
+            const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + 2 * i + 1], ac, -m_use));
+            pr[i] = bf16x2{static_cast<__bf16>(e0), static_cast<__bf16>(e1)};
+            lt = __builtin_amdgcn_fdot2_f32_bf16(pr[i], ones, lt, false);
+          }
+          p[kb][hf] = __builtin_bit_cast(bf16x8, pr);
+        }
+    };
+    // The reference is not kept at the running max: a tile's max is taken
+    // only while some lane has no reference yet (its keys so far were all
+    // masked, or none were seen), or when this tile's weights would take
+    // some lane's sum past kSumCap (a logit about 32 log2 units above the
+    // reference, or one that overflowed to inf).  Then every lane moves its
+    // reference to its own running max, rescales its state and computes the
+    // tile's weights again.  Otherwise no weight exceeds 2^32, and |O^T|
+    // stays within 2^33 max|V|.
+    const bool no_ref = __any(m_run == -INFINITY);
+    if (!no_ref) weights();
+    if (no_ref || __any(!(lt <= kSumCap))) {
+      // tile max: one chain per 32-key half, each step taking two logits
+      // (one v_max3), then the two lane halves through a lane-half swap
+      float hmax[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        hmax[kb] = fmaxf(s[kb][0], s[kb][1]);
+#pragma unroll
+        for (int r = 2; r < 16; r += 2) hmax[kb] = fmaxf(fmaxf(hmax[kb], s[kb][r]), s[kb][r + 1]);
+      }
+      float tmax = fmaxf(hmax[0], hmax[1]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                         __float_as_uint(tmax), false, false);
+        tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // running max in log2 units (ac > 0 keeps the arg-max); maxima below
+      // kMaskedLog2 are masked keys only
+      float tm = tmax * ac;
+      tm = tm > kMaskedLog2 ? tm : -INFINITY;
       const float m_new = fmaxf(m_run, tm);
       // 0 when nothing was accumulated yet; 1 for a lane whose max held
       const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -400,22 +435,10 @@ attn_bf16_kernel(
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       l_run *= alpha;
       m_run = m_new;
+      m_use = m_run == -INFINITY ? 0.0f : m_run;
+      weights();
     }
-    const float m_use = m_run == -INFINITY ? 0.0f : m_run;
-
-    // P^T = 2^(y - m) as bf16, already laid out as the PV B operand; the row
-    // maximum gets weight exactly 1
-    bf16x8 p[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(s[kb][8 * hf + i], ac, -m_use));
-          l_run += e;
-          p[kb][hf][i] = static_cast<__bf16>(e);
-        }
+    l_run = lt;
 
     // O^T += V^T P^T: k-step (kb, hf) covers keys 32kb + 16hf + {4hh..4hh+3,
     // 8+4hh..8+4hh+3}, stored at slots 32kb + 16hf + 8hh .. +7: one 16-byte read
