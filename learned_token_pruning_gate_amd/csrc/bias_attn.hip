@@ -124,9 +124,8 @@ __device__ __forceinline__ int bias_slot(int key) {
 // workgroup walks every key tile of its row while most CUs have finished.
 // The split cuts row p's key tiles [0, row_tiles(p)) into chunks of C tiles
 // (items), and packs the items into at most one workgroup per resident slot
-// (bins): full chunks get a bin each, the remainders and the short rows are
-// packed several to a bin, largest first.  A bin walks its items one after
-// the other.  An item of a row with more than one chunk writes its
+// (bins): largest first, each item to the bin with the least work so far.
+// A bin walks its items one after the other.  An item of a row with more than one chunk writes its
 // unnormalised softmax state (running max, sum, O^T) to the workspace, and
 // attn_merge_kernel combines a row's chunks; the other items write their
 // output directly.  Launching no more workgroups than the chip holds at once
@@ -749,9 +748,10 @@ constexpr int64_t kTwoStreamMaxGrid = 1024;
 constexpr int kMinChunkTiles = 4;
 // Cost model, in units of one key tile of one workgroup (~2.4 us at head
 // dim 128 with two workgroups per CU): each item adds its setup (Q and first
-// tile loads) and epilogue; the merge costs a launch plus the chunk states'
-// bytes read back at about 10 MB per unit.
-constexpr double kItemUnits = 1.5;
+// tile loads) and epilogue, two units (with one and a half, the packing chose
+// more and smaller chunks at N = 1500 that measured slower); the merge costs
+// a launch plus the chunk states' bytes read back at about 10 MB per unit.
+constexpr double kItemUnits = 2.0;
 // A two-stream workgroup's round of two tiles (one per stream) costs about
 // one unit, as measured with direct-to-LDS staging.
 constexpr double kTwoStreamRoundUnits = 1.0;
@@ -823,12 +823,12 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
   struct Item {
     int size, p, c;
   };
-  std::vector<Item> full, rest;
+  std::vector<Item> items;
+  std::vector<std::vector<uint16_t>> bins;
   for (int C = std::max((nt_max + kMaxChunks - 1) / kMaxChunks, kMinChunkTiles); C < nt_max;
        ++C) {
     const int nchunk = (nt_max + C - 1) / C;
-    full.clear();
-    rest.clear();
+    items.clear();
     int split_rows = 0;
     int64_t states = 0;   // chunk states written and merged, per query-head group
     for (int p = npb - 1; p >= 0; --p) {
@@ -837,35 +837,28 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
         ++split_rows;
         states += (nt + C - 1) / C;
       }
-      for (int c = 0; c * C < nt; ++c) {
-        const int size = std::min(C, nt - c * C);
-        (size == C ? full : rest).push_back(Item{size, p, c});
-      }
+      for (int c = 0; c * C < nt; ++c) items.push_back(Item{std::min(C, nt - c * C), p, c});
     }
-    if (full.size() + rest.size() > static_cast<size_t>(kMaxItems)) continue;
-    // full chunks first, then the rest largest first (ties: longer row first)
-    std::stable_sort(rest.begin(), rest.end(),
+    if (items.size() > static_cast<size_t>(kMaxItems)) continue;
+    // longest processing time first: items largest first (ties: longer row
+    // first), each to the bin with the least work so far (ties: lowest bin)
+    std::stable_sort(items.begin(), items.end(),
                      [](const Item& a, const Item& b) { return a.size > b.size; });
-    std::vector<Item> order(full);
-    order.insert(order.end(), rest.begin(), rest.end());
-    // next-fit packing into the fewest-cost bins that number at most max_bins
-    std::vector<uint16_t> first;
-    double cap = C + kItemUnits, makespan = 0.0;
-    for (;; cap += 0.25) {
-      first.assign(1, 0);
-      double fill = 0.0;
-      makespan = 0.0;
-      for (size_t i = 0; i < order.size(); ++i) {
-        const double cost = order[i].size + kItemUnits;
-        if (fill > 0.0 && fill + cost > cap) {
-          first.push_back(static_cast<uint16_t>(i));
-          fill = 0.0;
-        }
-        fill += cost;
-        makespan = std::max(makespan, fill);
-      }
-      first.push_back(static_cast<uint16_t>(order.size()));
-      if (static_cast<int>(first.size()) - 1 <= max_bins) break;
+    using Load = std::pair<double, int>;
+    std::priority_queue<Load, std::vector<Load>, std::greater<Load>> load;
+    for (int b = 0; b < max_bins; ++b) load.push(Load(0.0, b));
+    bins.assign(max_bins, {});
+    for (size_t i = 0; i < items.size(); ++i) {
+      Load l = load.top();
+      load.pop();
+      bins[l.second].push_back(static_cast<uint16_t>(i));
+      l.first += items[i].size + kItemUnits;
+      load.push(l);
+    }
+    double makespan = 0.0;
+    while (!load.empty()) {
+      makespan = std::max(makespan, load.top().first);
+      load.pop();
     }
     const double t = makespan + kMergeFixedUnits +
                      static_cast<double>(states * nhg) * state_bytes / kMergeBytesPerUnit;
@@ -873,12 +866,16 @@ SplitPlan make_split_plan(int64_t N, int64_t Hq, int64_t Hkv, int64_t D, bool ca
       best = t;
       best_plan.ctiles = C;
       best_plan.nchunk = nchunk;
-      best_plan.n_bins = static_cast<int32_t>(first.size()) - 1;
       best_plan.n_split_rows = split_rows;
-      best_plan.bin_first = first;
+      best_plan.bin_first.assign(1, 0);
       best_plan.items.clear();
-      for (const Item& it : order)
-        best_plan.items.push_back(static_cast<uint16_t>((it.p << 3) | it.c));
+      for (const auto& bin : bins) {
+        if (bin.empty()) continue;   // fewer items than bins
+        for (uint16_t i : bin)
+          best_plan.items.push_back(static_cast<uint16_t>((items[i].p << 3) | items[i].c));
+        best_plan.bin_first.push_back(static_cast<uint16_t>(best_plan.items.size()));
+      }
+      best_plan.n_bins = static_cast<int32_t>(best_plan.bin_first.size()) - 1;
     }
   }
   if (best_plan.ctiles == 0) return best_plan;
