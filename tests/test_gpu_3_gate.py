@@ -115,13 +115,13 @@ def test_gate_bf16_stream_cases(T, d, h, with_b1, frac, packed):
 
 
 @pytest.mark.parametrize("T,d,with_b1,frac", [
-    (65613, 2048, True, 0.8),   # 128-row tiles, 32-stage kernel, ragged last tile
     (66000, 1088, False, 0.6),  # 128-row tiles, 17 stages (the ring wraps partway)
 ])
 @pytest.mark.parametrize("packed", [False, True])
 def test_gate_bf16_stream_128_rows(T, d, with_b1, frac, packed):
-    """At h = 256, prompts long enough for two rounds of 128-row workgroups
-    on every CU take 128-row tiles: every row against the oracle."""
+    """At h = 256 and a hidden size other than 2048, prompts long enough for
+    two rounds of 128-row workgroups on every CU take 128-row tiles: every
+    row against the oracle."""
     args = _random_case(T, d, 256, False, with_b1, frac)
     got = run_gpu(*args, stride_pad=8 if T % 2 else 0, packed=packed)
     ref = run_oracle(*args)
@@ -133,11 +133,13 @@ def test_gate_bf16_stream_128_rows(T, d, with_b1, frac, packed):
 @pytest.mark.parametrize("T,d,with_b1,frac", [
     (33001, 2048, True, 0.8),   # two 64-row workgroups per CU, 32-stage kernel, ragged tail
     (40000, 1088, False, 0.6),  # the same, 17 stages (the ring wraps partway)
+    (65613, 2048, True, 0.8),   # 32-stage kernel above the 128-row threshold, ragged tail
 ])
 @pytest.mark.parametrize("packed", [False, True])
 def test_gate_bf16_stream_two_per_cu(T, d, with_b1, frac, packed):
     """At h = 256, prompts with two rounds of 64-row workgroups per CU but
-    not two of 128-row ones (32768 < T < 65409 on 256 CUs) run two
+    not two of 256-row ones at hidden size 2048 (or not two of 128-row ones
+    at other sizes; 32705 <= T < 130817 or 65409 on 256 CUs) run two
     workgroups on each CU at a time: against the oracle on the first and
     last rows, every workgroup's first and last rows, and random rows."""
     args = _random_case(T, d, 256, False, with_b1, frac)
