@@ -240,7 +240,10 @@ tg_status tg_compact_gather(tg_dtype dt, int64_t T, int64_t N, int64_t d,
  * finite, except key_score, which may be -inf (the key is deleted); a NaN
  * anywhere gives unspecified results (the kernels are built assuming none).
  *
- * dt            TG_DTYPE_BF16 (bf16 MFMA, fp32 softmax) or TG_DTYPE_F32.
+ * dt            TG_DTYPE_BF16 (bf16 MFMA, fp32 softmax; the weights are
+ *               rounded to bf16 for the PV product and the normaliser sums
+ *               those rounded weights, so lse carries their rounding, about
+ *               4e-3 at most) or TG_DTYPE_F32.
  * N             kept tokens, 0 <= N <= 2^31 - 1 (N == 0 is a no-op).
  * Hq, Hkv       query / KV heads, Hkv >= 1, Hq % Hkv == 0.
  * D             head dim: 64, 128 or 256 (ai.info summary "Main Findings":
