@@ -212,10 +212,10 @@ def test_attn_workspace_size(lib):
     size = lambda *a: lib.tg_bias_attn_workspace_size(*a)
     # N = 2512, 8/2 heads, D = 256, causal: 4 query heads per KV head, so 79
     # rows of 32 queries (row p has ceil(32 (p + 1) / 64) key tiles) x 2 head
-    # groups; the plan cuts rows into chunks of 15 tiles, so rows 30..78 (49
-    # rows) are split, with state slots for 3 chunks per head group: 49 x 3 x
+    # groups; the plan cuts rows into chunks of 14 tiles, so rows 28..78 (51
+    # rows) are split, with state slots for 3 chunks per head group: 51 x 3 x
     # 2 slots of 4 waves x (8 x 16 x 64 fp16 of O^T + 128 floats of max, sum)
-    assert size(BF16, 2512, 8, 2, 256, 1) == 49 * 3 * 2 * 4 * (8 * 16 * 64 * 2 + 128 * 4)
+    assert size(BF16, 2512, 8, 2, 256, 1) == 51 * 3 * 2 * 4 * (8 * 16 * 64 * 2 + 128 * 4)
     # the same prompt at 16/8 heads, D = 128: with fp16 chunk states the split
     # is priced below the two-stream launch
     assert size(BF16, 2512, 16, 8, 128, 1) > 0
