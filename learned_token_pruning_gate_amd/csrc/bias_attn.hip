@@ -750,12 +750,14 @@ constexpr int kMinChunkTiles = 4;
 // dim 128 with two workgroups per CU): each item adds its setup (Q and first
 // tile loads) and epilogue, two units (with one and a half, the packing chose
 // more and smaller chunks at N = 1500 that measured slower); the merge costs
-// a launch plus the chunk states' bytes read back at about 10 MB per unit.
+// two units for its launch (with one, N = 3000 at 16/8 heads split and
+// measured 55.6 against 52.1 us unsplit) plus the chunk states' bytes read
+// back at about 10 MB per unit.
 constexpr double kItemUnits = 2.0;
 // A two-stream workgroup's round of two tiles (one per stream) costs about
 // one unit, as measured with direct-to-LDS staging.
 constexpr double kTwoStreamRoundUnits = 1.0;
-constexpr double kMergeFixedUnits = 1.0;
+constexpr double kMergeFixedUnits = 2.0;
 constexpr double kMergeBytesPerUnit = 10.0e6;
 // The split must beat the unsplit launch by this factor to be used.
 constexpr double kSplitGain = 0.92;
