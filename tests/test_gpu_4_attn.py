@@ -380,25 +380,29 @@ def test_attn_small_q_scale_deletes_keys(entry):
                      "attn_small_qscale_lse_" + entry)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,causal", [
+    (8, 4, 128, True), (8, 4, 128, False), (8, 2, 256, True), (8, 4, 64, False)])
 @pytest.mark.parametrize("entry", ["unsplit", "split"])
-def test_attn_rising_logits_move_the_reference(entry):
+def test_attn_rising_logits_move_the_reference(entry, Hq, Hkv, D, causal):
     """Logits that keep rising along the keys move the softmax reference many
     times within a row: scores grow by 0.05 per key (about 180 log2 units
     over the prompt at gain 1), so the weights against a reference taken
     early pass 2^32 every few tiles, and one key's score jumps by 150 so
     that its weight overflows fp32 against any earlier reference.  Every
-    row against the oracle."""
-    rng = np.random.default_rng(97)
-    N, Hq, Hkv, D = 2512, 8, 4, 128
+    row against the oracle, causal and not, at head dims 64, 128 and 256
+    (every shape here also splits)."""
+    rng = np.random.default_rng(97 + D + (1 if causal else 0))
+    N = 2512
     q, k, v, _, g, c = make(rng, N, Hq, Hkv, D, "bf16")
     s = (0.05 * np.arange(N) + 0.3 * rng.standard_normal(N)).astype(np.float32)
     s[1500] += 150.0
     g = rng.uniform(0.8, 1.2, size=Hq).astype(np.float32)
     if entry == "split":
-        o, lse = gpu_split(q, k, v, s, g, c)
+        o, lse = gpu_split(q, k, v, s, g, c, causal=causal)
     else:
-        o, lse = gpu(q, k, v, s, g, c, "bf16")
-    ro, rl = ref(q, k, v, s, g, c, "bf16")
+        o, lse = gpu(q, k, v, s, g, c, "bf16", causal=causal)
+    ro, rl = ref(q, k, v, s, g, c, "bf16", causal=causal)
+    name = "attn_rising_%s_D%d_c%d" % (entry, D, causal)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    assert_close_abs(as_f64(o), ro, BF16_ABS, "attn_rising_" + entry)
-    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, "attn_rising_lse_" + entry)
+    assert_close_abs(as_f64(o), ro, BF16_ABS, name)
+    assert_close_abs(lse.cpu().numpy(), rl, LSE_ABS_BF16, name + "_lse")
