@@ -414,6 +414,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gate_bf16_stream_kernel(
 
   // residual blocks wave*XPW + i: row tile (block >> 1), k half (block & 1).
   // Rows past T re-read row T-1 (valid memory); their scores are never stored.
+  static_assert(XPW <= 4, "residual blocks per wave: xsrc holds four");
   const uint16_t* xsrc[4];   // XPW <= 4 (a fixed size: the direct-load builtin rejects a dependent type)
 #pragma unroll
   for (int i = 0; i < XPW; ++i) {
