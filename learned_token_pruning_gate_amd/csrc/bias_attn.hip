@@ -740,7 +740,11 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(
 // Two key streams per workgroup halve each wave's serial key loop, at the
 // cost of a whole CU's LDS per workgroup: they pay off while the grid is too
 // small to keep every CU busy with one-stream workgroups for several rounds.
-constexpr int64_t kTwoStreamMaxGrid = 1024;
+// Measured at 16/8 heads (grid = 8 ceil(N / 64)), unsplit: two streams took
+// 116 / 130 us at N = 4500 / 5000 against 133 / 140 us for 8-wave one-stream
+// workgroups, the same at 6000, and 217 / 272 / 282 us at 7000 / 8000 / 8192
+// against 200 / 251 / 259 us.
+constexpr int64_t kTwoStreamMaxGrid = 768;
 // Workgroups resident at once on the chip (its compute units, 256 on
 // MI355X, read from the device): two per CU for the one-stream kernel at
 // head dim <= 128, one per CU for two-stream workgroups and at head dim 256
